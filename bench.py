@@ -1,0 +1,268 @@
+"""Benchmark of the balanced expert-parallel hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic router output:
+moonep_plan -> moonep_dispatch -> moonep_combine (-> moonep_reduce_grad when the workload
+carries replica gradients).  The expert between dispatch and combine is the identity
+(y = recv), so combine reads exactly what dispatch wrote.
+
+Default workload: DeepSeek-V3-shaped, R=8 simulated ranks, E=256, K=8, S=4096 tokens per
+rank, H=7168 bf16, 32 prefetch slots per rank, router imbalance swept over maxvio
+0.2 / 1 / 5 / 20; the timed steps cycle through the four batches.
+
+value = algorithmic dispatch+combine bytes of the timed steps / wall time of the timed
+steps (plan included).  Algorithmic bytes per token: dispatch (K+1)*2H + 4K (read x and
+K row indices, write K rows), combine (K+1)*2H + 8K (read K rows, K indices and K
+weights, write one row); padding rows are not counted.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E, vendor figure
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dispatch_bytes(T, K, H):
+    return T * (K + 1) * 2 * H + T * 4 * K
+
+
+def combine_bytes(T, K, H):
+    return T * (K + 1) * 2 * H + T * 8 * K
+
+
+def reduce_bytes(plan_pieces, G_el):
+    # per expert with n slot replicas: read home + n replicas, write home
+    per = {}
+    for (e, r, slot) in plan_pieces:
+        if slot >= 0:
+            per[e] = per.get(e, 0) + 1
+    return sum((n + 2) * 4 * G_el for n in per.values())
+
+
+def cpu_baseline(wl, ids_np, w_np, x_np, budget_s=12.0):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    from oracle import moonep_oracle as O
+
+    t0 = time.perf_counter()
+    p = O.plan(ids_np, wl.R, wl.E, wl.K, wl.S, wl.slots)
+    dst = O.slot_map(p, ids_np)
+    t_plan = time.perf_counter() - t0
+    rows_total = wl.R * p.sz.NvS
+
+    def run(n):
+        d = dst[:n]
+        t = time.perf_counter()
+        recv = O.dispatch(d, x_np[:n], rows_total)
+        t1 = time.perf_counter()
+        O.combine(d, w_np[:n], recv)
+        t2 = time.perf_counter()
+        return t1 - t, t2 - t1
+
+    probe = min(128, wl.T)
+    td, tc = run(probe)
+    n = int(min(wl.T, max(probe, probe * budget_s / max(td + tc, 1e-6))))
+    td, tc = run(n)
+    nbytes = dispatch_bytes(n, wl.K, wl.H) + combine_bytes(n, wl.K, wl.H)
+    return {
+        "value": round(nbytes / (td + tc) / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"oracle plan+slot map on the full maxvio={wl.maxvio[0]} batch "
+                  f"({t_plan * 1e3:.1f} ms), then dispatch+combine of its first {n} of "
+                  f"{wl.T} tokens ({td:.2f} s + {tc:.2f} s); numpy, 1 thread",
+        "plan_ms": round(t_plan * 1e3, 2),
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: R expert-parallel ranks are simulated as HBM "
+              "partitions of a single MI355X, and nothing here uses a second GPU "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import combine_top_id_amd as M
+    from gen import BY_NAME, make_routing, make_hidden, make_grads, bf16_bits
+
+    wl = BY_NAME[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    log(f"workload {wl.name}: R={wl.R} E={wl.E} K={wl.K} S={wl.S} H={wl.H} slots={wl.slots} "
+        f"maxvio={wl.maxvio}")
+
+    batches = []
+    for mi, mv in enumerate(wl.maxvio):
+        ids, w, alpha, got = make_routing(wl.R, wl.E, wl.K, wl.S, mv, wl.seed(mi), device=dev)
+        x = make_hidden(wl.T, wl.H, wl.seed(mi) + 1, device=dev)
+        batches.append(dict(maxvio=mv, achieved=got, ids=ids, w=w, x=x))
+        log(f"  batch maxvio={mv}: achieved {got:.3f}")
+
+    sz = M.moonep_query(wl.R, wl.E, wl.K, wl.S, wl.slots)
+    recv = torch.empty(sz.recv_rows, wl.H, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(wl.T, wl.H, dtype=torch.bfloat16, device=dev)
+    home = rep = None
+    if wl.G_el:
+        home, rep = make_grads(wl.E, wl.R, wl.slots, wl.G_el, wl.seed(0) + 3, device=dev)
+    plan = None
+    stream = torch.cuda.current_stream()
+
+    def step(b, ev=None):
+        nonlocal plan
+        if ev: ev[0].record(stream)
+        plan = M.moonep_plan(b["ids"], b["w"], wl.R, wl.E, wl.K, wl.S, wl.slots, plan=plan)
+        if ev: ev[1].record(stream)
+        M.moonep_dispatch(plan, b["x"], recv)
+        if ev: ev[2].record(stream)
+        M.moonep_combine(plan, recv, out)
+        if ev: ev[3].record(stream)
+        if home is not None:
+            M.moonep_reduce_grad(plan, home, rep)
+            if ev: ev[4].record(stream)
+
+    nb = len(batches)
+    stats = []
+    for b in batches:
+        step(b)
+        stats.append(M.moonep_plan_status(plan))
+        b["pieces"] = [tuple(int(v) for v in q[:3])
+                       for q in plan.array("pieces", plan.sz.P_max * 8).view(-1, 8)
+                       [:stats[-1]["n_pieces"]].cpu().tolist()]
+    for s in range(args.warmup):
+        step(batches[s % nb])
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    nev = 5 if home is not None else 4
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(batches[s % nb], events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"timed {args.steps} steps in {wall * 1e3:.2f} ms")
+
+    per = [dict(plan=[], disp=[], comb=[], red=[]) for _ in range(nb)]
+    for s in range(args.steps):
+        ev = events[s]
+        d = per[s % nb]
+        d["plan"].append(ev[0].elapsed_time(ev[1]) * 1e3)
+        d["disp"].append(ev[1].elapsed_time(ev[2]) * 1e3)
+        d["comb"].append(ev[2].elapsed_time(ev[3]) * 1e3)
+        if home is not None:
+            d["red"].append(ev[3].elapsed_time(ev[4]) * 1e3)
+
+    db = dispatch_bytes(wl.T, wl.K, wl.H)
+    cb = combine_bytes(wl.T, wl.K, wl.H)
+    rows = []
+    for b, d, st in zip(batches, per, stats):
+        td, tc = statistics.median(d["disp"]), statistics.median(d["comb"])
+        row = dict(maxvio=b["maxvio"], achieved_maxvio=round(b["achieved"], 3),
+                   plan_us=round(statistics.median(d["plan"]), 2),
+                   dispatch_us=round(td, 2), combine_us=round(tc, 2),
+                   dispatch_gbps=round(db / td / 1e3, 1), combine_gbps=round(cb / tc / 1e3, 1),
+                   dc_gbps=round((db + cb) / (td + tc) / 1e3, 1),
+                   n_replicas=st["n_replicas"], n_fallback=st["n_fallback"],
+                   max_pieces_per_rank=st["max_pieces_per_rank"])
+        if home is not None:
+            tr = statistics.median(d["red"])
+            rb = reduce_bytes(b["pieces"], wl.G_el)
+            row.update(reduce_us=round(tr, 2), reduce_gbps=round(rb / tr / 1e3, 1))
+        rows.append(row)
+
+    all_d = [v for d in per for v in d["disp"]]
+    all_c = [v for d in per for v in d["comb"]]
+    mean_d, mean_c = statistics.mean(all_d), statistics.mean(all_c)
+    if mean_c >= mean_d:
+        dom, dom_bytes, dom_us = "combine", cb, mean_c
+    else:
+        dom, dom_bytes, dom_us = "dispatch", db, mean_d
+    achieved = dom_bytes / dom_us / 1e3
+    dc_times = [r["dispatch_us"] + r["combine_us"] for r in rows]
+
+    # a plain device copy of 4 GiB as a measured ceiling on the same box
+    a = torch.empty(1 << 31, dtype=torch.int16, device=dev)
+    c = torch.empty_like(a)
+    c.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        c.copy_(a)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 5 * 2 * a.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, c
+
+    value = args.steps * (db + cb) / wall / 1e9
+    res = {
+        "metric": "dispatch+combine GB/s & % HBM peak; plan µs, across maxvio 0.2–20",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: R={wl.R} simulated ranks, E={wl.E}, K={wl.K}, "
+                        f"S={wl.S} tokens/rank, H={wl.H} bf16, slots={wl.slots}, maxvio "
+                        f"sweep {'/'.join(str(m) for m in wl.maxvio)} (steps cycle through "
+                        f"the batches); identity expert",
+            "R": wl.R, "E": wl.E, "K": wl.K, "S": wl.S, "H": wl.H, "slots": wl.slots,
+            "tokens": wl.T, "accumulate": "fp32",
+        },
+        "pct_hbm_peak": round(100 * value / PEAK_HBM_GBPS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dom,
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": None,
+        },
+        "per_maxvio": rows,
+        "flatness_max_over_min": round(max(dc_times) / min(dc_times), 4),
+        "plan_us_median": round(statistics.median([r["plan_us"] for r in rows]), 2),
+        "copy_ceiling_gbps": round(copy_gbps, 1),
+    }
+    if not args.no_cpu_baseline:
+        b0 = batches[0]
+        log("cpu baseline (oracle) ...")
+        res["cpu_baseline"] = cpu_baseline(wl, b0["ids"].cpu().numpy(), b0["w"].cpu().numpy(),
+                                           bf16_bits(b0["x"]))
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,7 @@
+"""MI355X-native balanced expert-parallel hot path: plan -> zero-copy dispatch ->
+weighted combine -> replica-gradient reduce, as HIP kernels behind a C ABI
+(include/moonep.h, libmoonep.so), with a thin ctypes binding."""
+
+from .moonep import (moonep_query, moonep_plan, moonep_dispatch, moonep_combine,  # noqa: F401
+                     moonep_reduce_grad, moonep_plan_status, Plan, Sizes, MoonepError, lib,
+                     LIB_PATH, EXPORTS)

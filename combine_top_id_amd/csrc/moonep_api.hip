@@ -1,0 +1,123 @@
+// The C ABI: argument checks, sizes, and the launches on the caller's stream.
+#include <cstring>
+
+#include "moonep_internal.h"
+
+using namespace moonep;
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_desc(const moonep_plan_desc* d) {
+  if (!d || d->magic != kMagic || !d->dev) return MOONEP_EPLAN;
+  moonep_sizes s;
+  if (fill_sizes(d->sz.R, d->sz.E, d->sz.K, d->sz.S, d->sz.slots, &s) != MOONEP_OK)
+    return MOONEP_EPLAN;
+  if (std::memcmp(&s, &d->sz, sizeof(s)) != 0) return MOONEP_EPLAN;
+  return MOONEP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moonep_query(int R, int E, int K, int S, int slots, moonep_sizes* out) {
+  if (!out) return MOONEP_EINVAL;
+  moonep_sizes s;
+  std::memset(&s, 0, sizeof(s));
+  const int rc = fill_sizes(R, E, K, S, slots, &s);
+  if (rc != MOONEP_OK) return rc;
+  *out = s;
+  return MOONEP_OK;
+}
+
+int moonep_plan(const int32_t* topk_ids, const float* topk_w, int R, int E, int K, int S,
+                int slots, void* plan_dev, void* workspace, moonep_plan_desc* desc,
+                hipStream_t stream) {
+  if (!topk_ids || !topk_w || !plan_dev || !workspace || !desc) return MOONEP_EINVAL;
+  moonep_sizes s;
+  std::memset(&s, 0, sizeof(s));
+  const int rc = fill_sizes(R, E, K, S, slots, &s);
+  if (rc != MOONEP_OK) return rc;
+  if (!aligned(plan_dev, 256) || !aligned(workspace, 256) || !aligned(topk_ids, 4) ||
+      !aligned(topk_w, 4))
+    return MOONEP_EALIGN;
+  desc->magic = kMagic;
+  desc->sz = s;
+  desc->dev = plan_dev;
+  const hipError_t err = launch_plan(s, topk_ids, topk_w, static_cast<int32_t*>(plan_dev),
+                                     static_cast<int32_t*>(workspace), stream);
+  return err == hipSuccess ? MOONEP_OK : MOONEP_EHIP;
+}
+
+int moonep_dispatch(const moonep_plan_desc* plan, const uint16_t* x, int H, uint16_t* recv,
+                    hipStream_t stream) {
+  const int rc = check_desc(plan);
+  if (rc != MOONEP_OK) return rc;
+  if (!x || !recv || H <= 0 || H % 8 != 0) return MOONEP_EINVAL;
+  if (!aligned(x, 16) || !aligned(recv, 16)) return MOONEP_EALIGN;
+  const hipError_t err = launch_dispatch(plan->sz, static_cast<const int32_t*>(plan->dev), x,
+                                         H, recv, stream);
+  return err == hipSuccess ? MOONEP_OK : MOONEP_EHIP;
+}
+
+int moonep_combine(const moonep_plan_desc* plan, const uint16_t* y, int H, uint16_t* out,
+                   hipStream_t stream) {
+  const int rc = check_desc(plan);
+  if (rc != MOONEP_OK) return rc;
+  if (!y || !out || H <= 0 || H % 8 != 0) return MOONEP_EINVAL;
+  if (!aligned(y, 16) || !aligned(out, 16)) return MOONEP_EALIGN;
+  const hipError_t err = launch_combine(plan->sz, static_cast<const int32_t*>(plan->dev), y, H,
+                                        out, stream);
+  return err == hipSuccess ? MOONEP_OK : MOONEP_EHIP;
+}
+
+int moonep_reduce_grad(const moonep_plan_desc* plan, float* home_grad, const float* rep_grad,
+                       int64_t G_el, hipStream_t stream) {
+  const int rc = check_desc(plan);
+  if (rc != MOONEP_OK) return rc;
+  if (!home_grad || G_el < 0 || G_el % 4 != 0) return MOONEP_EINVAL;
+  if (plan->sz.slots > 0 && !rep_grad) return MOONEP_EINVAL;
+  if (!aligned(home_grad, 16) || (rep_grad && !aligned(rep_grad, 16))) return MOONEP_EALIGN;
+  if (G_el == 0 || plan->sz.slots == 0) return MOONEP_OK;
+  const hipError_t err = launch_reduce(plan->sz, static_cast<const int32_t*>(plan->dev),
+                                       home_grad, rep_grad, G_el, stream);
+  return err == hipSuccess ? MOONEP_OK : MOONEP_EHIP;
+}
+
+int moonep_plan_status(const moonep_plan_desc* plan, moonep_plan_stats* out,
+                       hipStream_t stream) {
+  const int rc = check_desc(plan);
+  if (rc != MOONEP_OK) return rc;
+  if (!out) return MOONEP_EINVAL;
+  if (hipStreamSynchronize(stream) != hipSuccess) return MOONEP_EHIP;
+  int32_t hdr[H_WORDS];
+  if (hipMemcpy(hdr, static_cast<const int32_t*>(plan->dev) + plan->sz.o_hdr, sizeof(hdr),
+                hipMemcpyDeviceToHost) != hipSuccess)
+    return MOONEP_EHIP;
+  out->status = hdr[H_STATUS];
+  out->bad_index = hdr[H_STATUS] == 1 ? hdr[H_BADIDX] : -1;
+  out->n_pieces = hdr[H_NPIECES];
+  out->n_replicas = hdr[H_NREPLICAS];
+  out->n_fallback = hdr[H_NFALLBACK];
+  out->max_pieces_per_rank = hdr[H_MAXPPR];
+  out->n_red = hdr[H_NRED];
+  out->n_shed = hdr[H_NSHED];
+  out->max_load = hdr[H_MAXLOAD];
+  return MOONEP_OK;
+}
+
+const char* moonep_strerror(int code) {
+  switch (code) {
+    case MOONEP_OK: return "ok";
+    case MOONEP_EINVAL: return "invalid argument";
+    case MOONEP_ELIMIT: return "sizes beyond the library's limits";
+    case MOONEP_EPLAN: return "plan descriptor missing, uninitialised or inconsistent";
+    case MOONEP_EHIP: return "HIP launch or copy failed";
+    case MOONEP_EALIGN: return "pointer not aligned (16 bytes for data, 256 for plan/workspace)";
+    default: return "unknown error";
+  }
+}
+
+}  // extern "C"

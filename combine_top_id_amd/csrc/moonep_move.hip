@@ -1,0 +1,276 @@
+// Data movement of the balanced expert-parallel step: zero-copy dispatch, weighted
+// combine, replica-gradient reduce.  All three are HBM-bound streams with no reuse
+// between workgroups: 16-byte vector loads and stores, non-temporal hints on the big
+// streams, and many bytes in flight per CU.
+//
+// "MoonshotAI/MoonEP 딥다이브" (fiv.co.kr), section 2, point 2: token rows go straight
+// to their final expert position and the buffer is handed to expert compute as a view,
+// with no permute or staging copy; section 4, pattern 3: replica gradients are summed
+// into their home expert.
+#include "moonep_internal.h"
+
+namespace moonep {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf_lo(unsigned int v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf_hi(unsigned int v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN -> 0x7FC0.
+__device__ __forceinline__ unsigned int to_bf16(float f) {
+  const unsigned int u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------------------------------
+// dispatch: recv[dst_row[t, k]] = x[t]
+// ---------------------------------------------------------------------------------------
+// One workgroup per token: each thread loads U vectors of the row, then stores them to
+// each of the token's K destination rows.
+template <int U>
+__global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* __restrict__ dst,
+                                                       const u32x4* __restrict__ x,
+                                                       u32x4* __restrict__ recv, int K,
+                                                       int nvec, int nrows) {
+  const int64_t t = blockIdx.x;
+  const int32_t* d = dst + t * K;
+  const u32x4* src = x + t * nvec;
+  const int step = blockDim.x * U;
+  for (int v0 = threadIdx.x; v0 < nvec; v0 += step) {
+    u32x4 buf[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int v = v0 + u * blockDim.x;
+      if (v < nvec) buf[u] = __builtin_nontemporal_load(src + v);
+    }
+    for (int k = 0; k < K; ++k) {
+      const int row = d[k];
+      if ((unsigned)row >= (unsigned)nrows) continue;   // -1: unmapped
+      u32x4* o = recv + (int64_t)row * nvec;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + u * blockDim.x;
+        if (v < nvec) __builtin_nontemporal_store(buf[u], o + v);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// combine: out[t] = bf16( sum_k w[t,k] * y[dst_row[t,k]] ), fp32, k ascending, no FMA
+// ---------------------------------------------------------------------------------------
+// acc += w * y[row, v0 + u*blockDim.x] for the thread's U vectors (8 bf16 each): a
+// separate fp32 multiply and add per element, in the caller's k order.
+template <int U>
+__device__ __forceinline__ void combine_accumulate(float (&acc)[U][8], const u32x4* __restrict__ y,
+                                                   int row, float wk, int v0, int nvec,
+                                                   int nrows) {
+  if ((unsigned)row >= (unsigned)nrows) return;    // -1: unmapped
+  const u32x4* src = y + (int64_t)row * nvec;
+  u32x4 yv[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int v = v0 + u * blockDim.x;
+    yv[u] = v < nvec ? __builtin_nontemporal_load(src + v) : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const unsigned int bits = yv[u][q];
+      const float p0 = wk * bf_lo(bits);
+      const float p1 = wk * bf_hi(bits);
+      acc[u][2 * q] = acc[u][2 * q] + p0;
+      acc[u][2 * q + 1] = acc[u][2 * q + 1] + p1;
+    }
+  }
+}
+
+template <int KT, int U>
+__global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ dst,
+                                                      const float* __restrict__ wts,
+                                                      const u32x4* __restrict__ y,
+                                                      u32x4* __restrict__ out, int Krt,
+                                                      int nvec, int nrows) {
+  const int K = KT > 0 ? KT : Krt;
+  const int64_t t = blockIdx.x;
+  const int32_t* d = dst + t * K;
+  const float* wt = wts + t * K;
+  const int step = blockDim.x * U;
+  for (int v0 = threadIdx.x; v0 < nvec; v0 += step) {
+    float acc[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[u][j] = 0.f;
+    if constexpr (KT > 0) {
+#pragma unroll
+      for (int k = 0; k < KT; ++k)
+        combine_accumulate<U>(acc, y, d[k], wt[k], v0, nvec, nrows);
+    } else {
+      for (int k = 0; k < K; ++k)
+        combine_accumulate<U>(acc, y, d[k], wt[k], v0, nvec, nrows);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int v = v0 + u * blockDim.x;
+      if (v < nvec) {
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          o[q] = to_bf16(acc[u][2 * q]) | (to_bf16(acc[u][2 * q + 1]) << 16);
+        __builtin_nontemporal_store(o, out + t * nvec + v);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// reduce: home[e] += rep[r_p][slot_p] for each slot piece p of e, in creation order
+// ---------------------------------------------------------------------------------------
+// A persistent grid walks (expert with replicas, chunk) items; the item count lives on
+// the device (plan header), so the host never waits for the plan.
+constexpr int kRedThreads = 256;
+constexpr int kRedU = 4;                       // float4 per thread per item
+constexpr int kRedChunk = kRedThreads * kRedU; // float4 per item
+
+__global__ __launch_bounds__(kRedThreads) void reduce_kernel(const int32_t* __restrict__ plan,
+                                                             f32x4* __restrict__ home,
+                                                             const f32x4* __restrict__ rep,
+                                                             int64_t g4, const moonep_sizes s) {
+  const int nred = plan[s.o_hdr + H_STATUS] == 0 ? plan[s.o_hdr + H_NRED] : 0;
+  const int64_t nchunk = (g4 + kRedChunk - 1) / kRedChunk;
+  const int64_t items = (int64_t)nred * nchunk;
+  const int32_t* red = plan + s.o_red;
+  const int32_t* pieces = plan + s.o_pieces;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int ri = (int)(it / nchunk);
+    const int64_t c = it - (int64_t)ri * nchunk;
+    const int e = red[ri];
+    if ((unsigned)e >= (unsigned)s.E) continue;
+    const int q0 = plan[s.o_pfirst + e];
+    const int q1 = q0 + plan[s.o_pnum + e];
+    f32x4* h = home + (int64_t)e * g4;
+    f32x4 acc[kRedU];
+#pragma unroll
+    for (int u = 0; u < kRedU; ++u) {
+      const int64_t v = c * kRedChunk + u * kRedThreads + threadIdx.x;
+      acc[u] = v < g4 ? h[v] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int q = q0; q < q1; ++q) {
+      const int slot = pieces[(int64_t)q * kPieceInts + P_SLOT];
+      if (slot < 0) break;                 // an expert's fallback pieces come last
+      const int r = pieces[(int64_t)q * kPieceInts + P_R];
+      if (slot >= s.slots || (unsigned)r >= (unsigned)s.R) break;
+      const f32x4* src = rep + ((int64_t)r * s.slots + slot) * g4;
+#pragma unroll
+      for (int u = 0; u < kRedU; ++u) {
+        const int64_t v = c * kRedChunk + u * kRedThreads + threadIdx.x;
+        if (v < g4) acc[u] = acc[u] + __builtin_nontemporal_load(src + v);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kRedU; ++u) {
+      const int64_t v = c * kRedChunk + u * kRedThreads + threadIdx.x;
+      if (v < g4) h[v] = acc[u];
+    }
+  }
+}
+
+// threads per workgroup and vectors per thread for a row of nvec 16-byte vectors:
+// the fewest idle lanes, then the most threads.
+void row_shape(int nvec, int umax, int* threads, int* u) {
+  int best_t = 64, best_u = 1;
+  long best_waste = -1;
+  for (int t : {256, 192, 128, 64}) {
+    int uu = (nvec + t - 1) / t;
+    if (uu > umax) uu = umax;
+    const long cover = (long)t * uu;
+    const long iters = (nvec + cover - 1) / cover;
+    const long waste = iters * cover - nvec;
+    if (best_waste < 0 || waste < best_waste) { best_waste = waste; best_t = t; best_u = uu; }
+  }
+  *threads = best_t;
+  *u = best_u;
+}
+
+template <int U>
+void launch_dispatch_u(const moonep_sizes& s, const int32_t* dst, const uint16_t* x,
+                       uint16_t* recv, int nvec, int threads, hipStream_t st) {
+  hipLaunchKernelGGL(dispatch_kernel<U>, dim3((unsigned)s.T), dim3(threads), 0, st, dst,
+                     reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(recv), s.K,
+                     nvec, (int)s.recv_rows);
+}
+
+template <int KT, int U>
+void launch_combine_ku(const moonep_sizes& s, const int32_t* dst, const float* w,
+                       const uint16_t* y, uint16_t* out, int nvec, int threads, hipStream_t st) {
+  hipLaunchKernelGGL((combine_kernel<KT, U>), dim3((unsigned)s.T), dim3(threads), 0, st, dst,
+                     w, reinterpret_cast<const u32x4*>(y), reinterpret_cast<u32x4*>(out), s.K,
+                     nvec, (int)s.recv_rows);
+}
+
+template <int KT>
+void launch_combine_k(const moonep_sizes& s, const int32_t* dst, const float* w,
+                      const uint16_t* y, uint16_t* out, int nvec, int threads, int u,
+                      hipStream_t st) {
+  switch (u) {
+    case 1: launch_combine_ku<KT, 1>(s, dst, w, y, out, nvec, threads, st); break;
+    case 2: launch_combine_ku<KT, 2>(s, dst, w, y, out, nvec, threads, st); break;
+    case 3: launch_combine_ku<KT, 3>(s, dst, w, y, out, nvec, threads, st); break;
+    default: launch_combine_ku<KT, 4>(s, dst, w, y, out, nvec, threads, st); break;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const moonep_sizes& s, const int32_t* plan, const uint16_t* x,
+                           int H, uint16_t* recv, hipStream_t st) {
+  const int nvec = H / 8;
+  int threads, u;
+  row_shape(nvec, 8, &threads, &u);
+  const int32_t* dst = plan + s.o_dst_row;
+  switch (u) {
+    case 1: launch_dispatch_u<1>(s, dst, x, recv, nvec, threads, st); break;
+    case 2: launch_dispatch_u<2>(s, dst, x, recv, nvec, threads, st); break;
+    case 3: launch_dispatch_u<3>(s, dst, x, recv, nvec, threads, st); break;
+    case 4: launch_dispatch_u<4>(s, dst, x, recv, nvec, threads, st); break;
+    case 5: launch_dispatch_u<5>(s, dst, x, recv, nvec, threads, st); break;
+    case 6: launch_dispatch_u<6>(s, dst, x, recv, nvec, threads, st); break;
+    case 7: launch_dispatch_u<7>(s, dst, x, recv, nvec, threads, st); break;
+    default: launch_dispatch_u<8>(s, dst, x, recv, nvec, threads, st); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const moonep_sizes& s, const int32_t* plan, const uint16_t* y,
+                          int H, uint16_t* out, hipStream_t st) {
+  const int nvec = H / 8;
+  int threads, u;
+  row_shape(nvec, 4, &threads, &u);
+  const int32_t* dst = plan + s.o_dst_row;
+  const float* w = reinterpret_cast<const float*>(plan + s.o_w);
+  switch (s.K) {
+    case 1: launch_combine_k<1>(s, dst, w, y, out, nvec, threads, u, st); break;
+    case 2: launch_combine_k<2>(s, dst, w, y, out, nvec, threads, u, st); break;
+    case 4: launch_combine_k<4>(s, dst, w, y, out, nvec, threads, u, st); break;
+    case 6: launch_combine_k<6>(s, dst, w, y, out, nvec, threads, u, st); break;
+    case 8: launch_combine_k<8>(s, dst, w, y, out, nvec, threads, u, st); break;
+    default: launch_combine_k<0>(s, dst, w, y, out, nvec, threads, u, st); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce(const moonep_sizes& s, const int32_t* plan, float* home,
+                         const float* rep, int64_t G_el, hipStream_t st) {
+  const int64_t g4 = G_el / 4;
+  hipLaunchKernelGGL(reduce_kernel, dim3(2048), dim3(kRedThreads), 0, st, plan,
+                     reinterpret_cast<f32x4*>(home), reinterpret_cast<const f32x4*>(rep), g4,
+                     s);
+  return hipGetLastError();
+}
+
+}  // namespace moonep

@@ -1,0 +1,205 @@
+"""Thin ctypes binding of libmoonep.so (the C ABI in include/moonep.h).
+
+Argument marshalling only: torch tensors supply device pointers and the current HIP
+stream; every step of the path runs in the library's HIP kernels.  There is no CPU
+fallback: if the library is not built, or no GPU is present, calls raise.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoonep.so")
+
+MOONEP_OK = 0
+ROW_ALIGN = 16
+
+
+class MoonepError(RuntimeError):
+    pass
+
+
+class Sizes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("R", "E", "K", "S", "slots", "E_loc", "C", "G",
+                                              "NvS", "P_max")] + \
+               [(n, ctypes.c_int64) for n in ("T", "A", "recv_rows", "plan_bytes",
+                                              "workspace_bytes")] + \
+               [(n, ctypes.c_int32) for n in ("nblk", "blk")] + \
+               [(n, ctypes.c_int64) for n in ("o_hdr", "o_load", "o_shed", "o_keep",
+                                              "o_home_row", "o_pfirst", "o_pnum", "o_pieces",
+                                              "o_slot_expert", "o_off", "o_red", "o_dst_row",
+                                              "o_w")]
+
+
+class PlanDesc(ctypes.Structure):
+    _fields_ = [("magic", ctypes.c_uint32), ("sz", Sizes), ("dev", ctypes.c_void_p)]
+
+
+class PlanStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("status", "bad_index", "n_pieces", "n_replicas",
+                                              "n_fallback", "max_pieces_per_rank", "n_red",
+                                              "n_shed", "max_load")]
+
+
+_lib = None
+
+
+def lib():
+    """Load libmoonep.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise MoonepError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    L.moonep_query.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(Sizes)]
+    L.moonep_plan.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, ctypes.POINTER(PlanDesc), vp]
+    L.moonep_dispatch.argtypes = [ctypes.POINTER(PlanDesc), vp, i32, vp, vp]
+    L.moonep_combine.argtypes = [ctypes.POINTER(PlanDesc), vp, i32, vp, vp]
+    L.moonep_reduce_grad.argtypes = [ctypes.POINTER(PlanDesc), vp, vp, i64, vp]
+    L.moonep_plan_status.argtypes = [ctypes.POINTER(PlanDesc), ctypes.POINTER(PlanStats), vp]
+    L.moonep_strerror.argtypes = [i32]
+    L.moonep_strerror.restype = ctypes.c_char_p
+    for f in ("moonep_query", "moonep_plan", "moonep_dispatch", "moonep_combine",
+              "moonep_reduce_grad", "moonep_plan_status"):
+        getattr(L, f).restype = i32
+    _lib = L
+    return L
+
+
+EXPORTS = ("moonep_query", "moonep_plan", "moonep_dispatch", "moonep_combine",
+           "moonep_reduce_grad", "moonep_plan_status", "moonep_strerror")
+
+
+def _check(rc):
+    if rc != MOONEP_OK:
+        raise MoonepError(f"moonep error {rc}: {lib().moonep_strerror(rc).decode()}")
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise MoonepError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise MoonepError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise MoonepError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def moonep_query(R, E, K, S, slots) -> Sizes:
+    s = Sizes()
+    _check(lib().moonep_query(R, E, K, S, slots, ctypes.byref(s)))
+    return s
+
+
+class Plan:
+    """A plan: host descriptor + the device blob it describes (+ its workspace)."""
+
+    def __init__(self, sizes, blob, workspace):
+        self.sz = sizes
+        self.blob = blob
+        self.workspace = workspace
+        self.desc = PlanDesc()
+
+    @property
+    def NvS(self):
+        return self.sz.NvS
+
+    def array(self, name, count):
+        """A view of one int32 array of the device blob (offset field `o_<name>`)."""
+        o = getattr(self.sz, "o_" + name)
+        return self.blob[o:o + count]
+
+    @property
+    def dst_row(self):
+        return self.array("dst_row", self.sz.A).view(self.sz.T, self.sz.K)
+
+    @property
+    def weights(self):
+        return self.array("w", self.sz.A).view(torch.float32).view(self.sz.T, self.sz.K)
+
+
+def _blob(nbytes, device):
+    # int32 elements; torch's caching allocator returns 256-byte aligned blocks
+    t = torch.empty((nbytes + 3) // 4, dtype=torch.int32, device=device)
+    assert t.data_ptr() % 256 == 0
+    return t
+
+
+def moonep_plan(topk_ids, topk_w, R, E, K, S, slots, plan=None, stream=None) -> Plan:
+    """Enqueue the planning kernels; returns the Plan (reusable by dispatch, combine and
+    reduce).  Pass `plan` to reuse its blob and workspace (same sizes)."""
+    sz = moonep_query(R, E, K, S, slots)
+    ids_p = _dev(topk_ids, torch.int32, "topk_ids")
+    w_p = _dev(topk_w, torch.float32, "topk_w")
+    if topk_ids.numel() != sz.A or topk_w.numel() != sz.A:
+        raise MoonepError("topk_ids / topk_w must hold R*S*K elements")
+    if plan is None or plan.sz.plan_bytes != sz.plan_bytes or \
+            plan.sz.workspace_bytes != sz.workspace_bytes:
+        plan = Plan(sz, _blob(sz.plan_bytes, topk_ids.device),
+                    _blob(sz.workspace_bytes, topk_ids.device))
+    plan.sz = sz
+    _check(lib().moonep_plan(ids_p, w_p, R, E, K, S, slots,
+                             ctypes.c_void_p(plan.blob.data_ptr()),
+                             ctypes.c_void_p(plan.workspace.data_ptr()),
+                             ctypes.byref(plan.desc), _stream(stream)))
+    return plan
+
+
+def moonep_dispatch(plan: Plan, x, recv=None, stream=None):
+    """recv[dst_row[t, k]] = x[t]; x is bf16 [T, H]; returns recv bf16 [R*NvS, H]."""
+    H = x.shape[-1]
+    if x.numel() != plan.sz.T * H:
+        raise MoonepError("x must be [T, H]")
+    if recv is None:
+        recv = torch.empty(plan.sz.recv_rows, H, dtype=torch.bfloat16, device=x.device)
+    if recv.numel() != plan.sz.recv_rows * H:
+        raise MoonepError("recv must be [R*NvS, H]")
+    _check(lib().moonep_dispatch(ctypes.byref(plan.desc), _dev(x, torch.bfloat16, "x"), H,
+                                 _dev(recv, torch.bfloat16, "recv"), _stream(stream)))
+    return recv
+
+
+def moonep_combine(plan: Plan, y, out=None, stream=None):
+    """out[t] = bf16(sum_k w[t,k] * y[dst_row[t,k]]); y bf16 [R*NvS, H] -> out bf16 [T, H]."""
+    H = y.shape[-1]
+    if y.numel() != plan.sz.recv_rows * H:
+        raise MoonepError("y must be [R*NvS, H]")
+    if out is None:
+        out = torch.empty(plan.sz.T, H, dtype=torch.bfloat16, device=y.device)
+    if out.numel() != plan.sz.T * H:
+        raise MoonepError("out must be [T, H]")
+    _check(lib().moonep_combine(ctypes.byref(plan.desc), _dev(y, torch.bfloat16, "y"), H,
+                                _dev(out, torch.bfloat16, "out"), _stream(stream)))
+    return out
+
+
+def moonep_reduce_grad(plan: Plan, home_grad, rep_grad, stream=None):
+    """home_grad[e] += replica slabs of e (in place); home fp32 [E, G_el], rep fp32
+    [R, slots, G_el]."""
+    G_el = home_grad.shape[-1]
+    if home_grad.numel() != plan.sz.E * G_el:
+        raise MoonepError("home_grad must be [E, G_el]")
+    if rep_grad.numel() != plan.sz.R * plan.sz.slots * G_el:
+        raise MoonepError("rep_grad must be [R, slots, G_el]")
+    rep_p = _dev(rep_grad, torch.float32, "rep_grad") if rep_grad.numel() else ctypes.c_void_p(0)
+    _check(lib().moonep_reduce_grad(ctypes.byref(plan.desc),
+                                    _dev(home_grad, torch.float32, "home_grad"), rep_p, G_el,
+                                    _stream(stream)))
+    return home_grad
+
+
+def moonep_plan_status(plan: Plan, stream=None) -> dict:
+    """Wait for the stream, then return the plan's statistics."""
+    st = PlanStats()
+    _check(lib().moonep_plan_status(ctypes.byref(plan.desc), ctypes.byref(st), _stream(stream)))
+    return {n: getattr(st, n) for n, _ in PlanStats._fields_}

@@ -1,0 +1,158 @@
+/*
+ * moonep.h -- C ABI of the balanced expert-parallel hot path on one MI355X (gfx950).
+ *
+ * R expert-parallel ranks are simulated as partitions of one GPU's HBM.  One MoE layer
+ * step runs four calls, in the order the pages give for a forward and backward pass
+ * ("MoonshotAI/MoonEP 딥다이브" (fiv.co.kr), section 5: planning -> dispatch -> expert
+ * compute -> combine -> grad_reduce):
+ *
+ *   moonep_plan        live top-K router output -> replica plan + token->row map
+ *   moonep_dispatch    zero-copy scatter of bf16 token rows into static per-rank buffers
+ *   moonep_combine     weighted gather of expert outputs back to token order
+ *   moonep_reduce_grad replica gradients summed into their home experts
+ *
+ * Notation.  T = R*S tokens; token t comes from rank t / S.  Assignment i = t*K + k.
+ * E_loc = E/R experts per rank; expert e is homed on rank e / E_loc.  C = S*K is every
+ * rank's exact quota ("Moonshot AI Open-Sources MoonEP" (tldrocket.com), paragraph 3).
+ * G = E_loc + slots groups per rank.  NvS = align16(C + G*15) rows per rank buffer
+ * (S*K plus alignment padding: deep dive, section 4, design pattern 2).
+ *
+ * Conventions for every call:
+ *   - Device pointers are plain HIP device addresses; the caller owns and allocates all
+ *     memory.  The library never allocates, frees or synchronises (except
+ *     moonep_plan_status, which waits on `stream`).
+ *   - All GPU work is enqueued on `stream` (0 = the null stream) and is asynchronous.
+ *   - Return value: MOONEP_OK (0) or a negative MOONEP_E* code.  On an error return
+ *     nothing was enqueued.  Data errors found on the device (an expert id outside
+ *     [0, E)) are never reported by a return code: they set the plan's status word,
+ *     read with moonep_plan_status; such a plan maps nothing (every dst_row is -1),
+ *     dispatch then writes nothing, combine writes zero rows and reduce adds nothing.
+ *   - Calls are thread-safe; the library has no global mutable state.
+ */
+#ifndef MOONEP_H_
+#define MOONEP_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOONEP_ROW_ALIGN 16      /* rows: each home/slot group starts on a multiple */
+#define MOONEP_MAX_R 64          /* the planner keeps one wave64 lane per rank      */
+#define MOONEP_MAX_E 1024
+#define MOONEP_MAX_K 32
+#define MOONEP_MAX_SLOTS 256
+
+enum {
+  MOONEP_OK = 0,
+  MOONEP_EINVAL = -1,   /* a size or pointer argument is invalid                       */
+  MOONEP_ELIMIT = -2,   /* sizes beyond MOONEP_MAX_* or int32 row indexing              */
+  MOONEP_EPLAN = -3,    /* the plan descriptor is not initialised or does not match     */
+  MOONEP_EHIP = -4,     /* a HIP launch or copy failed                                  */
+  MOONEP_EALIGN = -5    /* a data pointer is not 16-byte aligned                        */
+};
+
+/* Sizes of one (R, E, K, S, slots) problem; filled by moonep_query (host only). */
+typedef struct moonep_sizes {
+  int32_t R, E, K, S, slots;
+  int32_t E_loc, C, G, NvS, P_max;
+  int64_t T, A;
+  int64_t recv_rows;        /* R * NvS: rows of the dispatch buffer [R, NvS, H]          */
+  int64_t plan_bytes;       /* device bytes of the plan blob                             */
+  int64_t workspace_bytes;  /* device bytes of the transient workspace of moonep_plan    */
+  int32_t nblk, blk;        /* assignment blocks used by the plan kernels                */
+  /* int32-element offsets of the plan blob's arrays (for inspection and tests):        */
+  int64_t o_hdr, o_load, o_shed, o_keep, o_home_row, o_pfirst, o_pnum, o_pieces,
+          o_slot_expert, o_off, o_red, o_dst_row, o_w;
+} moonep_sizes;
+
+/* Host-side handle of a plan: sizes plus the caller's device blob.  Filled by
+ * moonep_plan; read by the other calls.  Copying the struct copies the handle. */
+typedef struct moonep_plan_desc {
+  uint32_t magic;
+  moonep_sizes sz;
+  void* dev;                /* device blob of sz.plan_bytes, 256-byte aligned            */
+} moonep_plan_desc;
+
+/* Plan statistics, copied from the device by moonep_plan_status. */
+typedef struct moonep_plan_stats {
+  int32_t status;           /* 0 = valid plan; 1 = an expert id was outside [0, E)       */
+  int32_t bad_index;        /* smallest assignment index with a bad id, else -1          */
+  int32_t n_pieces;         /* replica pieces (slot-backed + fallback)                   */
+  int32_t n_replicas;       /* slot-backed pieces = prefetch slots in use                */
+  int32_t n_fallback;       /* pieces served by cross-partition weight reads             */
+  int32_t max_pieces_per_rank;
+  int32_t n_red;            /* experts with at least one slot replica                    */
+  int32_t n_shed;           /* experts that shed assignments                             */
+  int32_t max_load;         /* largest per-expert load                                   */
+} moonep_plan_stats;
+
+/* Sizes for a problem, host only.  EINVAL unless R>=1, E%R==0, 1<=K<=E, S>=1, slots>=0;
+ * ELIMIT beyond R<=64, E<=1024, K<=32, slots<=256, or when R*NvS or T*K exceeds int32. */
+int moonep_query(int R, int E, int K, int S, int slots, moonep_sizes* out);
+
+/* Planning ("Moonshot AI Open-Sources MoonEP", paragraph 3: duplicate a few overloaded
+ * experts, planned from live router output, so every rank receives exactly S*K; deep
+ * dive, section 4, design pattern 1: plan once, reuse).
+ *
+ *   topk_ids   device int32 [T, K] row-major, ranks contiguous (token t from rank t/S)
+ *   topk_w     device fp32  [T, K]; copied into the plan, so combine needs no weights
+ *   plan_dev   device blob of moonep_sizes.plan_bytes, 256-byte aligned
+ *   workspace  device scratch of moonep_sizes.workspace_bytes, 256-byte aligned; free
+ *              for reuse once the plan's kernels have run on `stream`
+ *   desc       host handle, filled synchronously (sizes + plan_dev)
+ *
+ * The plan rule: experts are taken by (load descending, id ascending); an expert on a
+ * home whose load exceeds S*K sheds min(load, remaining excess); each shed assignment
+ * goes to the lowest-id rank still short of S*K that has a free prefetch slot, else
+ * (slots exhausted) to the lowest-id rank still short, as a fallback piece whose expert
+ * weights are read across partitions ("Moonshot AI Open-Sources MoonEP", paragraph 5).
+ * Within an expert, assignments are taken in increasing i: the home keeps the first
+ * `keep`, replica pieces take the rest in creation order.  Each rank's buffer holds its
+ * home experts, then its slots (each group 16-row aligned), then a fallback region.
+ * Deterministic: the same ids give a bit-identical plan. */
+int moonep_plan(const int32_t* topk_ids, const float* topk_w, int R, int E, int K, int S,
+                int slots, void* plan_dev, void* workspace, moonep_plan_desc* desc,
+                hipStream_t stream);
+
+/* Zero-copy dispatch ("MoonshotAI/MoonEP 딥다이브", section 2, point 2: each token row
+ * is written straight into its final expert position; no permute, no staging copy):
+ *   recv[dst_row[t, k], :] = x[t, :]  (bit copy) for every assignment.
+ *   x     device bf16 [T, H] (raw 16-bit patterns)      recv  device bf16 [R*NvS, H]
+ * H % 8 == 0; x and recv 16-byte aligned.  Padding rows of recv are not written. */
+int moonep_dispatch(const moonep_plan_desc* plan, const uint16_t* x, int H, uint16_t* recv,
+                    hipStream_t stream);
+
+/* Weighted combine (deep dive, section 1: dispatch -> expert compute -> combine):
+ *   out[t, :] = bf16_rne( sum_{k=0..K-1} w[t,k] * float(y[dst_row[t,k], :]) )
+ * accumulated in fp32, k ascending, each product and sum rounded separately (no fused
+ * multiply-add), one round-to-nearest-even to bf16 at the end.
+ *   y     device bf16 [R*NvS, H] (expert outputs, laid out like recv)
+ *   out   device bf16 [T, H]
+ * H % 8 == 0; y and out 16-byte aligned; out must not overlap y. */
+int moonep_combine(const moonep_plan_desc* plan, const uint16_t* y, int H, uint16_t* out,
+                   hipStream_t stream);
+
+/* Replica-gradient reduce (deep dive, section 4, design pattern 3: a replica's gradient
+ * is kept apart and added to its home expert, so training equals no replication):
+ *   for each expert e, for its slot pieces in creation order:
+ *       home_grad[e, :] += rep_grad[rank, slot, :]      (fp32 adds, in that order)
+ *   home_grad  device fp32 [E, G_el], updated in place
+ *   rep_grad   device fp32 [R, slots, G_el]
+ * G_el % 4 == 0; both 16-byte aligned.  Fallback pieces own no slot and add nothing. */
+int moonep_reduce_grad(const moonep_plan_desc* plan, float* home_grad, const float* rep_grad,
+                       int64_t G_el, hipStream_t stream);
+
+/* Waits for `stream`, then copies the plan's statistics to the host.  The only call
+ * that synchronises. */
+int moonep_plan_status(const moonep_plan_desc* plan, moonep_plan_stats* out,
+                       hipStream_t stream);
+
+const char* moonep_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOONEP_H_ */
