@@ -16,6 +16,7 @@ constexpr int kMapWaves = 8;                // waves per workgroup of the hist/m
 constexpr int kMapThreads = kMapWaves * 64;
 constexpr int kPlanThreads = 1024;          // the single planner workgroup
 constexpr int kPieceInts = 8;               // e, r, slot, cnt, start, fbpos, row0, pad
+constexpr int kMaxBlocks = 64;              // target number of assignment blocks
 
 // header words
 enum Hdr : int {
@@ -49,9 +50,10 @@ inline int fill_sizes(int R, int E, int K, int S, int slots, moonep_sizes* s) {
   s->T = T; s->A = A;
   s->recv_rows = NvS * R;
   // assignment blocks: kMapThreads * m assignments each, m a power of two in [1, 32],
-  // aiming at no more than about 128 blocks so the block-prefix work stays small.
+  // aiming at no more than kMaxBlocks blocks so the planner's per-expert block prefix
+  // stays one batch of loads per thread.
   int64_t m = 1;
-  while (m < 32 && (int64_t)kMapThreads * m * 128 < A) m *= 2;
+  while (m < 32 && (int64_t)kMapThreads * m * kMaxBlocks < A) m *= 2;
   s->blk = (int32_t)(kMapThreads * m);
   s->nblk = (int32_t)((A + s->blk - 1) / s->blk);
   int64_t o = 0;
@@ -69,16 +71,17 @@ inline int fill_sizes(int R, int E, int K, int S, int slots, moonep_sizes* s) {
   s->o_dst_row = o;     o += align64(A);
   s->o_w = o;           o += align64(A);
   s->plan_bytes = o * 4;
-  // workspace: per-block expert counts [nblk][E], per-block first bad index [nblk],
-  // slot piece sizes [R][slots]
+  // workspace: per-block expert counts [nblk][E] (overwritten by the planner with
+  // per-block bases), per-block first bad index [nblk], per-wave prefixes inside each
+  // block [nblk][kMapWaves][E]
   s->workspace_bytes = (align64((int64_t)s->nblk * E) + align64(s->nblk) +
-                        align64((int64_t)R * (slots > 0 ? slots : 1))) * 4;
+                        align64((int64_t)s->nblk * kMapWaves * E)) * 4;
   return MOONEP_OK;
 }
 
 // workspace offsets (int32 elements)
 __host__ __device__ inline int64_t ws_bad(const moonep_sizes& s) { return align64((int64_t)s.nblk * s.E); }
-__host__ __device__ inline int64_t ws_slotcnt(const moonep_sizes& s) { return ws_bad(s) + align64(s.nblk); }
+__host__ __device__ inline int64_t ws_sub(const moonep_sizes& s) { return ws_bad(s) + align64(s.nblk); }
 
 // Launchers (defined in the .hip files).
 hipError_t launch_plan(const moonep_sizes& s, const int32_t* ids, const float* w,

@@ -7,16 +7,20 @@
 // section 4, pattern 1: the plan is computed once and reused; pattern 2: static S*K
 // plus alignment padding buffers.
 //
-// Three launches on the caller's stream:
-//   1. hist_kernel     one workgroup per block of `blk` assignments: LDS histogram of
-//                      expert ids -> per-block counts, first invalid id per block.
-//   2. planner_kernel  one workgroup: expert loads, per-rank excess and deficit,
-//                      shedding, greedy placement (one wave, one lane per rank),
-//                      buffer layout, piece rows, statistics.
-//   3. map_kernel      one workgroup per block: the stable rank j of every assignment
-//                      among its expert's assignments (wave64 ballot peer masks plus
-//                      per-wave LDS counters and block prefixes), then its row;
-//                      also copies the top-K weights into the plan.
+// Assignments are cut into blocks of `blk` = kMapThreads * M; block b is counted by one
+// workgroup, whose wave w owns the contiguous sub-block of 64*M assignments starting at
+// b*blk + w*64*M.  Three launches on the caller's stream:
+//   1. hist_kernel     per block: one LDS histogram per wave -> the block's expert counts
+//                      and, per wave, the count of earlier waves of the block; the first
+//                      invalid id of the block.
+//   2. planner_kernel  one workgroup: per-block bases (exclusive scan of the counts over
+//                      blocks), expert loads, per-rank excess and deficit, shedding,
+//                      greedy placement (one wave, lane r = rank r), buffer layout
+//                      (one wave per rank), piece rows, statistics.  Everything stays in
+//                      LDS until one final write of the plan.
+//   3. map_kernel      one single-wave workgroup per sub-block: the stable rank j of each
+//                      assignment among its expert's assignments (ballot peer masks and an
+//                      LDS counter per expert), then its row; copies the top-K weights.
 #include <climits>
 
 #include "moonep_internal.h"
@@ -24,53 +28,81 @@
 namespace moonep {
 namespace {
 
-__device__ __forceinline__ int lane_id() { return __lane_id(); }
-
 __device__ __forceinline__ uint64_t lanemask_lt() {
-  const int l = lane_id();
+  const int l = __lane_id();
   return l == 0 ? 0ull : (~0ull >> (64 - l));
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// DPP controls (GFX9): shift right within a row of 16 lanes; broadcast lane 15 / 31.
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+// Inclusive prefix sum over the 64 lanes of a wave, in data-parallel-primitive moves:
+// four shifts inside each row of 16 lanes, then the row totals carried across rows.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int t = __shfl_up(v, d, 64);
-    if (l >= d) v += t;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, kRowShr1, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, kRowShr2, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, kRowShr4, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, kRowShr8, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, kRowBcast15, 0xa, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kRowBcast31, 0xc, 0xf, false);
   return v;
 }
 
+__device__ __forceinline__ int lane63(int v) { return __builtin_amdgcn_readlane(v, 63); }
+
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+__device__ __forceinline__ int align_rows(int n) { return (n + kRowAlign - 1) / kRowAlign * kRowAlign; }
 
 // ---------------------------------------------------------------------------------------
 // 1. per-block histogram
 // ---------------------------------------------------------------------------------------
+template <int M>
 __global__ __launch_bounds__(kMapThreads) void hist_kernel(const int32_t* __restrict__ ids,
                                                            int32_t* __restrict__ ws,
                                                            const moonep_sizes s) {
-  extern __shared__ int32_t lds[];
+  extern __shared__ int32_t lds[];          // [kMapWaves][E]
   __shared__ int bad;
   const int E = s.E;
-  const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += kMapThreads) lds[e] = 0;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t i_wave = (int64_t)blockIdx.x * s.blk + (int64_t)wave * (64 * M);
+  int idv[M];
+#pragma unroll
+  for (int c = 0; c < M; ++c) {
+    const int64_t i = i_wave + c * 64 + lane;
+    idv[c] = i < s.A ? ids[i] : 0;
+  }
+  int32_t* mine = lds + wave * E;
+  for (int e = lane; e < E; e += 64) mine[e] = 0;
   if (tid == 0) bad = INT_MAX;
   __syncthreads();
-  const int64_t i0 = (int64_t)blockIdx.x * s.blk;
-  const int64_t i1 = min(i0 + (int64_t)s.blk, s.A);
   int mybad = INT_MAX;
-  for (int64_t i = i0 + tid; i < i1; i += kMapThreads) {
-    const int id = ids[i];
-    if ((unsigned)id < (unsigned)E)
-      atomicAdd(&lds[id], 1);
-    else
-      mybad = min(mybad, (int)i);
+#pragma unroll
+  for (int c = 0; c < M; ++c) {
+    const int64_t i = i_wave + c * 64 + lane;
+    if (i < s.A) {
+      const int id = idv[c];
+      if ((unsigned)id < (unsigned)E)
+        atomicAdd(&mine[id], 1);
+      else
+        mybad = min(mybad, (int)i);
+    }
   }
   if (mybad != INT_MAX) atomicMin(&bad, mybad);
   __syncthreads();
   int32_t* cnt = ws + (int64_t)blockIdx.x * E;
-  for (int e = tid; e < E; e += kMapThreads) cnt[e] = lds[e];
+  int32_t* sub = ws + ws_sub(s) + (int64_t)blockIdx.x * kMapWaves * E;
+  for (int e = tid; e < E; e += kMapThreads) {
+    int acc = 0;
+#pragma unroll
+    for (int v = 0; v < kMapWaves; ++v) {
+      const int c = lds[v * E + e];
+      sub[v * E + e] = acc;
+      acc += c;
+    }
+    cnt[e] = acc;
+  }
   if (tid == 0) ws[ws_bad(s) + blockIdx.x] = bad;
 }
 
@@ -83,40 +115,87 @@ __device__ __forceinline__ bool before(int la, int a, int lb, int b) {
   return la > lb || (la == lb && a < b);
 }
 
+constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int kColRegs = 32;   // block counts a column thread keeps in registers
+
 __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restrict__ plan,
                                                                int32_t* __restrict__ ws,
                                                                const moonep_sizes s) {
   extern __shared__ int32_t lds[];
   const int E = s.E, R = s.R, E_loc = s.E_loc, C = s.C, slots = s.slots, G = s.G;
-  const int NvS = s.NvS;
+  const int NvS = s.NvS, PM = s.P_max;
   int32_t* load_s = lds;            // [E]
   int32_t* shed_s = load_s + E;     // [E]
   int32_t* keep_s = shed_s + E;     // [E]
   int32_t* order_s = keep_s + E;    // [E] shedding experts, plan order
-  int32_t* pfirst_s = order_s + E;  // [E]
+  int32_t* list_s = order_s + E;    // [E] shedding experts, id order
+  int32_t* pfirst_s = list_s + E;   // [E]
   int32_t* pnum_s = pfirst_s + E;   // [E]
-  __shared__ int32_t X_s[64], D_s[64], used_s[64], fb_s[64], nfb_s[64];
-  __shared__ int bad_s, nshed_s, npieces_s, maxload_s, err_s, nred_s;
+  int32_t* pe_s = pnum_s + E;             // pieces: expert, rank, slot, count, start,
+  int32_t* pr_s = pe_s + PM;              //   fallback position, first row   [P_max] each
+  int32_t* psl_s = pr_s + PM;
+  int32_t* pc_s = psl_s + PM;
+  int32_t* pst_s = pc_s + PM;
+  int32_t* pfb_s = pst_s + PM;
+  int32_t* prow_s = pfb_s + PM;
+  int32_t* part_s = pe_s;           // [kPlanThreads] column segment sums, used before the
+                                    // pieces exist
+  __shared__ int32_t hl_s[64], used_s[64], fb_s[64], nfb_s[64];
+  __shared__ int bad_s, nshed_s, npieces_s, maxload_s, err_s;
 
   int32_t* hdr = plan + s.o_hdr;
-  int32_t* pieces = plan + s.o_pieces;
-  int32_t* slot_expert = plan + s.o_slot_expert;
-  int32_t* off = plan + s.o_off;
-  int32_t* home_row = plan + s.o_home_row;
-  int32_t* slot_cnt = ws + ws_slotcnt(s);
   const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const uint64_t lt = lanemask_lt();
 
-  // ---- expert loads: column sums of the per-block counts --------------------------------
-  for (int e = tid; e < E; e += kPlanThreads) load_s[e] = 0;
-  if (tid == 0) { bad_s = INT_MAX; nshed_s = 0; maxload_s = 0; err_s = 0; }
-  __syncthreads();
-  {
-    const int64_t n = (int64_t)s.nblk * E;
-    for (int64_t f = tid; f < n; f += kPlanThreads) {
-      const int v = ws[f];
-      if (v) atomicAdd(&load_s[(int)(f % E)], v);
+  // ---- per-block bases and expert loads -----------------------------------------------------
+  // ws[b][e] holds block b's count of expert e.  Each column is split into `tpc` segments
+  // of consecutive blocks, one thread per (segment, expert): segment sums, then the
+  // exclusive scan over blocks, kept in registers and written back at the very end.
+  if (tid < 64) hl_s[tid] = 0;
+  if (tid == 0) { bad_s = INT_MAX; maxload_s = 0; err_s = 0; }
+  const int nblk = s.nblk;
+  int tpc = 1;
+  while (tpc * 2 * E <= kPlanThreads && tpc * 2 <= nblk) tpc *= 2;
+  const int seg = (nblk + tpc - 1) / tpc;
+  const bool col_thread = tid < tpc * E;
+  const int ce = tid % E, cg = tid / E;
+  const int b0 = cg * seg, b1 = min(b0 + seg, nblk);
+  const bool in_regs = seg <= kColRegs;
+  int v[kColRegs];
+  if (col_thread) {
+    int sum = 0;
+    if (in_regs) {
+#pragma unroll
+      for (int u = 0; u < kColRegs; ++u) v[u] = b0 + u < b1 ? ws[(int64_t)(b0 + u) * E + ce] : 0;
+#pragma unroll
+      for (int u = 0; u < kColRegs; ++u) sum += v[u];
+    } else {
+      for (int b = b0; b < b1; b += kColRegs) {
+        int w[kColRegs];
+#pragma unroll
+        for (int u = 0; u < kColRegs; ++u) w[u] = b + u < b1 ? ws[(int64_t)(b + u) * E + ce] : 0;
+#pragma unroll
+        for (int u = 0; u < kColRegs; ++u) sum += w[u];
+      }
     }
-    for (int b = tid; b < s.nblk; b += kPlanThreads) atomicMin(&bad_s, ws[ws_bad(s) + b]);
+    part_s[cg * E + ce] = sum;
+  }
+  // first invalid id per block (nblk <= kPlanThreads while blocks hold up to 32 chunks
+  // per wave; larger counts loop)
+  int mybad = INT_MAX;
+  for (int b = tid; b < nblk; b += kPlanThreads) mybad = min(mybad, ws[ws_bad(s) + b]);
+  __syncthreads();
+  if (mybad != INT_MAX) atomicMin(&bad_s, mybad);
+  int colbase = 0;   // the column thread's first base (blocks before b0)
+  if (col_thread) {
+    for (int g = 0; g < cg; ++g) colbase += part_s[g * E + ce];
+    if (cg == tpc - 1) {
+      const int total = colbase + part_s[cg * E + ce];
+      load_s[ce] = total;
+      atomicAdd(&hl_s[ce / E_loc], total);
+      atomicMax(&maxload_s, total);
+    }
   }
   __syncthreads();
 
@@ -124,38 +203,37 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
     // an expert id outside [0, E): publish an empty plan that maps nothing
     for (int e = tid; e < E; e += kPlanThreads) {
       plan[s.o_load + e] = 0; plan[s.o_shed + e] = 0; plan[s.o_keep + e] = 0;
-      plan[s.o_pfirst + e] = 0; plan[s.o_pnum + e] = 0; home_row[e] = -1;
+      plan[s.o_pfirst + e] = 0; plan[s.o_pnum + e] = 0; plan[s.o_home_row + e] = -1;
     }
-    if (tid < H_WORDS) hdr[tid] = 0;
-    __syncthreads();
-    if (tid == 0) {
-      hdr[H_MAGIC] = (int32_t)kMagic; hdr[H_STATUS] = 1; hdr[H_BADIDX] = bad_s;
-      hdr[H_R] = R; hdr[H_E] = E; hdr[H_K] = s.K; hdr[H_S] = s.S; hdr[H_SLOTS] = slots;
-      hdr[H_NVS] = NvS;
+    if (tid < H_WORDS) {
+      int val = 0;
+      switch (tid) {
+        case H_MAGIC: val = (int32_t)kMagic; break;
+        case H_STATUS: val = 1; break;
+        case H_BADIDX: val = bad_s; break;
+        case H_R: val = R; break;
+        case H_E: val = E; break;
+        case H_K: val = s.K; break;
+        case H_S: val = s.S; break;
+        case H_SLOTS: val = slots; break;
+        case H_NVS: val = NvS; break;
+        default: break;
+      }
+      hdr[tid] = val;
     }
     return;
   }
 
-  // ---- home loads, excess and deficit per rank --------------------------------------------
-  if (tid < 64) {
-    int hl = 0;
-    if (tid < R)
-      for (int g = 0; g < E_loc; ++g) hl += load_s[tid * E_loc + g];
-    X_s[tid] = tid < R ? max(0, hl - C) : 0;
-    D_s[tid] = tid < R ? max(0, C - hl) : 0;
-    used_s[tid] = 0; fb_s[tid] = 0; nfb_s[tid] = 0;
-  }
-  for (int e = tid; e < E; e += kPlanThreads) atomicMax(&maxload_s, load_s[e]);
-  __syncthreads();
-
   // ---- shed: an overloaded home gives away its heaviest experts first -----------------
-  for (int e = tid; e < E; e += kPlanThreads) {
+  if (tid < E) {                   // E <= kPlanThreads
+    const int e = tid;
     const int h = e / E_loc;
-    const int X = X_s[h];
+    const int X = max(0, hl_s[h] - C);
     const int le = load_s[e];
     int sh = 0;
     if (X > 0) {
       int ahead = 0;   // load of the home's experts that come before e
+#pragma unroll 8
       for (int e2 = h * E_loc; e2 < (h + 1) * E_loc; ++e2) {
         const int l2 = load_s[e2];
         if (before(l2, e2, le, e)) ahead += l2;
@@ -169,32 +247,41 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
   }
   __syncthreads();
 
-  // ---- shedding experts in (load desc, id asc) order ---------------------------------------
-  for (int e = tid; e < E; e += kPlanThreads) {
-    if (shed_s[e] > 0) {
-      const int le = load_s[e];
-      int pos = 0;
-      for (int e2 = 0; e2 < E; ++e2)
-        if (shed_s[e2] > 0 && before(load_s[e2], e2, le, e)) ++pos;
-      order_s[pos] = e;
-      atomicAdd(&nshed_s, 1);
+  // ---- wave 0: order the shedding experts, then place them --------------------------------
+  if (wave == 0) {
+    // shedding experts in id order (ballot compaction), then ranked by (load desc, id asc)
+    int n = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      const int e = e0 + lane;
+      const bool f = e < E && shed_s[e] > 0;
+      const uint64_t m = __ballot(f);
+      if (f) list_s[n + __popcll(m & lt)] = e;
+      n += __popcll(m);
     }
-  }
-  __syncthreads();
+    const int nshed = n;
+    for (int t0 = 0; t0 < nshed; t0 += 64) {
+      const int t = t0 + lane;
+      if (t < nshed) {
+        const int e = list_s[t];
+        const int le = load_s[e];
+        int rank = 0;
+        for (int j = 0; j < nshed; ++j) {
+          const int e2 = list_s[j];
+          rank += before(load_s[e2], e2, le, e) ? 1 : 0;
+        }
+        order_s[rank] = e;
+      }
+    }
 
-  // ---- placement: one wave, lane r holds rank r ------------------------------------------
-  // For one expert, the lowest-id ranks that are short and have a free slot are filled in
-  // id order until the expert's shed count is used up (each piece fills its receiver
-  // except possibly the last); any rest goes, again in id order, to ranks that are short
-  // but have no free slot (fallback pieces).  This is the one-assignment-at-a-time greedy
-  // done one expert at a time.
-  if (tid < 64) {
-    const int lane = tid;
-    int D = D_s[lane];
+    // Placement, lane r = rank r.  For one expert, the lowest-id ranks that are short and
+    // have a free slot are filled in id order until its shed count is used up (each piece
+    // fills its receiver except possibly the last); any rest goes, again in id order, to
+    // ranks that are short but have no free slot (fallback pieces).  This is the
+    // one-assignment-at-a-time greedy, done one expert at a time.
+    int D = lane < R ? max(0, C - hl_s[lane]) : 0;
     int used = 0, fbrows = 0, nfb = 0;
     int np = 0;
-    const int nshed = nshed_s;
-    const uint64_t lt = lanemask_lt();
+    bool err = false;
     for (int q = 0; q < nshed; ++q) {
       const int e = order_s[q];
       int rem = shed_s[e];
@@ -209,16 +296,16 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
         const uint64_t m = __ballot(take > 0);
         if (take > 0) {
           const int p = np + __popcll(m & lt);
-          int32_t* pc = pieces + (int64_t)min(p, s.P_max - 1) * kPieceInts;
-          if (p >= s.P_max) err_s = 1;
-          pc[P_E] = e; pc[P_R] = lane; pc[P_SLOT] = used; pc[P_CNT] = take;
-          pc[P_START] = start + excl; pc[P_FBPOS] = 0;
-          slot_expert[lane * slots + used] = e;
-          slot_cnt[lane * slots + used] = take;
+          if (p < PM) {
+            pe_s[p] = e; pr_s[p] = lane; psl_s[p] = used; pc_s[p] = take;
+            pst_s[p] = start + excl; pfb_s[p] = 0;
+          } else {
+            err = true;
+          }
           used += 1;
           D -= take;
         }
-        const int moved = min(rem, __shfl(incl, 63, 64));
+        const int moved = min(rem, lane63(incl));
         np += __popcll(m);
         rem -= moved;
         start += moved;
@@ -231,15 +318,17 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
         const uint64_t m = __ballot(take > 0);
         if (take > 0) {
           const int p = np + __popcll(m & lt);
-          int32_t* pc = pieces + (int64_t)min(p, s.P_max - 1) * kPieceInts;
-          if (p >= s.P_max) err_s = 1;
-          pc[P_E] = e; pc[P_R] = lane; pc[P_SLOT] = -1; pc[P_CNT] = take;
-          pc[P_START] = start + excl; pc[P_FBPOS] = fbrows;
+          if (p < PM) {
+            pe_s[p] = e; pr_s[p] = lane; psl_s[p] = -1; pc_s[p] = take;
+            pst_s[p] = start + excl; pfb_s[p] = fbrows;
+          } else {
+            err = true;
+          }
           fbrows += take;
           nfb += 1;
           D -= take;
         }
-        const int moved = min(rem, __shfl(incl, 63, 64));
+        const int moved = min(rem, lane63(incl));
         np += __popcll(m);
         rem -= moved;
         start += moved;
@@ -247,49 +336,70 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
       if (lane == 0) {
         pfirst_s[e] = first;
         pnum_s[e] = np - first;
-        if (rem != 0) err_s = 1;
       }
+      err = err || rem != 0;
     }
     used_s[lane] = used;
     fb_s[lane] = fbrows;
     nfb_s[lane] = nfb;
-    if (lane < R && D != 0) err_s = 1;
-    if (lane == 0) npieces_s = min(np, s.P_max);
+    if (__ballot(err || (lane < R && D != 0))) { if (lane == 0) err_s = 1; }
+    if (lane == 0) { npieces_s = min(np, PM); nshed_s = nshed; }
   }
   __syncthreads();
 
-  // ---- layout of each rank's buffer: home groups, slot groups, fallback region -----------
-  if (tid < R) {
-    const int r = tid;
-    int32_t* o = off + (int64_t)r * (G + 1);
-    int pos = 0;
-    for (int g = 0; g < E_loc; ++g) {
-      const int e = r * E_loc + g;
-      o[g] = pos;
-      home_row[e] = r * NvS + pos;
-      pos = (pos + keep_s[e] + kRowAlign - 1) / kRowAlign * kRowAlign;
-    }
-    const int u = used_s[r];
-    for (int sl = 0; sl < slots; ++sl) {
-      o[E_loc + sl] = pos;
-      int size = 0;
-      if (sl < u) size = slot_cnt[r * slots + sl];
-      else slot_expert[r * slots + sl] = -1;
-      pos = (pos + size + kRowAlign - 1) / kRowAlign * kRowAlign;
-    }
-    o[G] = pos;
-    if (pos + fb_s[r] > NvS) err_s = 1;
-  }
-  __syncthreads();
-
-  // ---- first row of every piece; per-expert tables -----------------------------------------
+  // ---- layout of each rank's buffer, one wave per rank --------------------------------------
+  // Home groups, then slot groups (slot order = the order the rank's slot pieces were
+  // created), then the fallback region; each home and slot group starts on a multiple of
+  // ROW_ALIGN rows.  The same scans give every piece its first row.
   const int np = npieces_s;
+  int32_t* off = plan + s.o_off;
+  int32_t* slot_expert = plan + s.o_slot_expert;
+  for (int r = wave; r < R; r += kPlanWaves) {
+    int32_t* o = off + (int64_t)r * (G + 1);
+    int carry = 0;
+    for (int g0 = 0; g0 < E_loc; g0 += 64) {
+      const int g = g0 + lane;
+      const int a = g < E_loc ? align_rows(keep_s[r * E_loc + g]) : 0;
+      const int incl = wave_incl_scan(a);
+      if (g < E_loc) {
+        o[g] = carry + incl - a;
+        plan[s.o_home_row + r * E_loc + g] = r * NvS + carry + incl - a;
+      }
+      carry += lane63(incl);
+    }
+    for (int p0 = 0; p0 < np; p0 += 64) {          // slot pieces of rank r
+      const int p = p0 + lane;
+      const bool mine = p < np && pr_s[p] == r && psl_s[p] >= 0;
+      const int a = mine ? align_rows(pc_s[p]) : 0;
+      const int incl = wave_incl_scan(a);
+      if (mine) {
+        const int row = carry + incl - a;
+        o[E_loc + psl_s[p]] = row;
+        slot_expert[r * slots + psl_s[p]] = pe_s[p];
+        prow_s[p] = r * NvS + row;
+      }
+      carry += lane63(incl);
+    }
+    for (int sl = used_s[r] + lane; sl < slots; sl += 64) {   // unused slots
+      o[E_loc + sl] = carry;
+      slot_expert[r * slots + sl] = -1;
+    }
+    if (lane == 0) {
+      o[G] = carry;
+      if (carry + fb_s[r] > NvS) err_s = 1;
+    }
+    for (int p0 = 0; p0 < np; p0 += 64) {          // fallback pieces of rank r
+      const int p = p0 + lane;
+      if (p < np && pr_s[p] == r && psl_s[p] < 0) prow_s[p] = r * NvS + carry + pfb_s[p];
+    }
+  }
+  __syncthreads();
+
+  // ---- write the plan ---------------------------------------------------------------------
   for (int p = tid; p < np; p += kPlanThreads) {
-    int32_t* pc = pieces + (int64_t)p * kPieceInts;
-    const int r = pc[P_R], slot = pc[P_SLOT];
-    const int32_t* o = off + (int64_t)r * (G + 1);
-    pc[P_ROW0] = r * NvS + (slot >= 0 ? o[E_loc + slot] : o[G] + pc[P_FBPOS]);
-    pc[7] = 0;
+    int32_t* pc = plan + s.o_pieces + (int64_t)p * kPieceInts;
+    pc[P_E] = pe_s[p]; pc[P_R] = pr_s[p]; pc[P_SLOT] = psl_s[p]; pc[P_CNT] = pc_s[p];
+    pc[P_START] = pst_s[p]; pc[P_FBPOS] = pfb_s[p]; pc[P_ROW0] = prow_s[p]; pc[7] = 0;
   }
   for (int e = tid; e < E; e += kPlanThreads) {
     plan[s.o_load + e] = load_s[e];
@@ -298,48 +408,77 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
     plan[s.o_pfirst + e] = pfirst_s[e];
     plan[s.o_pnum + e] = pnum_s[e];
   }
-  // experts with slot replicas, in plan order (the reduce work list)
-  if (tid < 64) {
-    const int lane = tid;
-    const uint64_t lt = lanemask_lt();
-    int n = 0;
+  if (col_thread) {
+    // per-block bases for the map kernel
+    int run = colbase;
+    if (in_regs) {
+#pragma unroll
+      for (int u = 0; u < kColRegs; ++u) {
+        if (b0 + u < b1) {
+          ws[(int64_t)(b0 + u) * E + ce] = run;
+          run += v[u];
+        }
+      }
+    } else {
+      for (int b = b0; b < b1; b += kColRegs) {
+        int w[kColRegs];
+#pragma unroll
+        for (int u = 0; u < kColRegs; ++u) w[u] = b + u < b1 ? ws[(int64_t)(b + u) * E + ce] : 0;
+#pragma unroll
+        for (int u = 0; u < kColRegs; ++u) {
+          if (b + u < b1) {
+            ws[(int64_t)(b + u) * E + ce] = run;
+            run += w[u];
+          }
+        }
+      }
+    }
+  }
+  if (wave == 0) {
+    // experts with slot replicas, in plan order (the reduce work list)
     const int nshed = nshed_s;
+    int n = 0;
     for (int q0 = 0; q0 < nshed; q0 += 64) {
       const int q = q0 + lane;
       bool has = false;
       int e = 0;
       if (q < nshed) {
         e = order_s[q];
-        has = pnum_s[e] > 0 && pieces[(int64_t)pfirst_s[e] * kPieceInts + P_SLOT] >= 0;
+        has = pnum_s[e] > 0 && psl_s[pfirst_s[e]] >= 0;
       }
       const uint64_t m = __ballot(has);
       if (has) plan[s.o_red + n + __popcll(m & lt)] = e;
       n += __popcll(m);
     }
-    if (lane == 0) nred_s = n;
-  }
-  __syncthreads();
-
-  if (tid == 0) {
-    int nrep = 0, nfb = 0, maxppr = 0;
-    for (int r = 0; r < R; ++r) {
-      nrep += used_s[r];
-      nfb += nfb_s[r];
-      maxppr = max(maxppr, used_s[r] + nfb_s[r]);
+    // statistics over ranks (lane r)
+    int nrep = used_s[lane], nfb = nfb_s[lane], ppr = used_s[lane] + nfb_s[lane];
+    for (int d = 32; d >= 1; d >>= 1) {
+      nrep += __shfl_xor(nrep, d, 64);
+      nfb += __shfl_xor(nfb, d, 64);
+      ppr = max(ppr, __shfl_xor(ppr, d, 64));
     }
-    for (int w = 0; w < H_WORDS; ++w) hdr[w] = 0;
-    hdr[H_MAGIC] = (int32_t)kMagic;
-    hdr[H_STATUS] = err_s ? 2 : 0;
-    hdr[H_NPIECES] = np;
-    hdr[H_NREPLICAS] = nrep;
-    hdr[H_NFALLBACK] = nfb;
-    hdr[H_MAXPPR] = maxppr;
-    hdr[H_NRED] = err_s ? 0 : nred_s;
-    hdr[H_BADIDX] = -1;
-    hdr[H_NSHED] = nshed_s;
-    hdr[H_MAXLOAD] = maxload_s;
-    hdr[H_R] = R; hdr[H_E] = E; hdr[H_K] = s.K; hdr[H_S] = s.S; hdr[H_SLOTS] = slots;
-    hdr[H_NVS] = NvS;
+    const bool err = err_s != 0;
+    int val = 0;
+    switch (lane) {
+      case H_MAGIC: val = (int32_t)kMagic; break;
+      case H_STATUS: val = err ? 2 : 0; break;
+      case H_NPIECES: val = np; break;
+      case H_NREPLICAS: val = nrep; break;
+      case H_NFALLBACK: val = nfb; break;
+      case H_MAXPPR: val = ppr; break;
+      case H_NRED: val = err ? 0 : n; break;
+      case H_BADIDX: val = -1; break;
+      case H_NSHED: val = nshed; break;
+      case H_MAXLOAD: val = maxload_s; break;
+      case H_R: val = R; break;
+      case H_E: val = E; break;
+      case H_K: val = s.K; break;
+      case H_S: val = s.S; break;
+      case H_SLOTS: val = slots; break;
+      case H_NVS: val = NvS; break;
+      default: break;
+    }
+    hdr[lane] = val;   // H_WORDS == 64: one word per lane
   }
 }
 
@@ -347,34 +486,51 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
 // 3. token -> row map
 // ---------------------------------------------------------------------------------------
 
-// M = chunks of 64 assignments per wave; a block is kMapThreads * M assignments.
+// One single-wave workgroup per sub-block of 64*M assignments (wave w of block b in the
+// histogram's numbering).  Every global load it needs is issued first: ids, weights,
+// the per-expert tables, the sub-block's base per expert (block base from the planner +
+// earlier waves of the block from the histogram), the piece table.
+constexpr int kTab = 8;   // table entries per lane loaded per round trip
+
+template <int M> struct MapGroup { static constexpr int value = M < 8 ? M : 8; };
+
 template <int M>
-__global__ __launch_bounds__(kMapThreads) void map_kernel(const int32_t* __restrict__ ids,
-                                                          const float* __restrict__ w,
-                                                          int32_t* __restrict__ plan,
-                                                          const int32_t* __restrict__ ws,
-                                                          const moonep_sizes s) {
+__global__ __launch_bounds__(64) void map_kernel(const int32_t* __restrict__ ids,
+                                                 const float* __restrict__ w,
+                                                 int32_t* __restrict__ plan,
+                                                 const int32_t* __restrict__ ws,
+                                                 const moonep_sizes s) {
   extern __shared__ int32_t lds[];
   const int E = s.E;
   const int P = s.P_max;
-  int32_t* run = lds;                       // [kMapWaves][E]
-  int32_t* keep_s = run + kMapWaves * E;    // [E]
-  int32_t* home_s = keep_s + E;             // [E]
-  int32_t* pfirst_s = home_s + E;           // [E]
-  int32_t* pnum_s = pfirst_s + E;           // [E]
-  int32_t* pstart_s = pnum_s + E;           // [P]
-  int32_t* pcnt_s = pstart_s + P;           // [P]
-  int32_t* prow_s = pcnt_s + P;             // [P]
+  int32_t* run = lds;                  // [E]  assignments of e before the current chunk
+  int32_t* keep_s = run + E;           // [E]
+  int32_t* home_s = keep_s + E;        // [E]
+  int32_t* pfirst_s = home_s + E;      // [E]
+  int32_t* pnum_s = pfirst_s + E;      // [E]
+  int32_t* pstart_s = pnum_s + E;      // [P]
+  int32_t* pcnt_s = pstart_s + P;      // [P]
+  int32_t* prow_s = pcnt_s + P;        // [P]
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
+  constexpr int kMapGroup = MapGroup<M>::value;   // chunks ranked per pass
+  const int lane = threadIdx.x;
+  const int b = blockIdx.x / kMapWaves, sw = blockIdx.x % kMapWaves;
   const int64_t A = s.A;
-  const int64_t i_wave = (int64_t)blockIdx.x * s.blk + (int64_t)wave * (64 * M);
+  const int64_t i_wave = (int64_t)b * s.blk + (int64_t)sw * (64 * M);
   int32_t* dst = plan + s.o_dst_row;
   float* wout = reinterpret_cast<float*>(plan + s.o_w);
+  if (i_wave >= A) return;
 
-  if (plan[s.o_hdr + H_STATUS] != 0) {
+  const int status = plan[s.o_hdr + H_STATUS];
+  int idv[M];
+  float wt[M];
+#pragma unroll
+  for (int c = 0; c < M; ++c) {
+    const int64_t i = i_wave + c * 64 + lane;
+    idv[c] = i < A ? ids[i] : E;    // E marks lanes past the end
+    wt[c] = i < A ? w[i] : 0.f;
+  }
+  if (status != 0) {
     // invalid plan: map nothing
 #pragma unroll
     for (int c = 0; c < M; ++c) {
@@ -383,93 +539,92 @@ __global__ __launch_bounds__(kMapThreads) void map_kernel(const int32_t* __restr
     }
     return;
   }
-
-  int idv[M];
-  float wv[M];
+  // tables to LDS, kTab entries per lane per round trip (loads first, then stores)
+  const int32_t* bbase = ws + (int64_t)b * E;
+  const int32_t* wbase = ws + ws_sub(s) + ((int64_t)b * kMapWaves + sw) * E;
+  for (int e0 = 0; e0 < E; e0 += 64 * kTab) {
+    int t0[kTab], t1[kTab], t2[kTab], t3[kTab], t4[kTab], t5[kTab];
 #pragma unroll
-  for (int c = 0; c < M; ++c) {
-    const int64_t i = i_wave + c * 64 + lane;
-    idv[c] = i < A ? ids[i] : E;    // E marks lanes past the end
-    wv[c] = i < A ? w[i] : 0.f;
-  }
-
-  for (int e = lane; e < E; e += 64) run[wave * E + e] = 0;
-  for (int e = tid; e < E; e += kMapThreads) {
-    keep_s[e] = plan[s.o_keep + e];
-    home_s[e] = plan[s.o_home_row + e];
-    pfirst_s[e] = plan[s.o_pfirst + e];
-    pnum_s[e] = plan[s.o_pnum + e];
+    for (int k = 0; k < kTab; ++k) {
+      const int e = e0 + k * 64 + lane;
+      if (e < E) {
+        t0[k] = bbase[e]; t1[k] = wbase[e]; t2[k] = plan[s.o_keep + e];
+        t3[k] = plan[s.o_home_row + e]; t4[k] = plan[s.o_pfirst + e]; t5[k] = plan[s.o_pnum + e];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kTab; ++k) {
+      const int e = e0 + k * 64 + lane;
+      if (e < E) {
+        run[e] = t0[k] + t1[k]; keep_s[e] = t2[k]; home_s[e] = t3[k];
+        pfirst_s[e] = t4[k]; pnum_s[e] = t5[k];
+      }
+    }
   }
   const int np = plan[s.o_hdr + H_NPIECES];
-  for (int p = tid; p < np; p += kMapThreads) {
-    const int32_t* pc = plan + s.o_pieces + (int64_t)p * kPieceInts;
-    pstart_s[p] = pc[P_START];
-    pcnt_s[p] = pc[P_CNT];
-    prow_s[p] = pc[P_ROW0];
+  for (int p0 = 0; p0 < np; p0 += 64 * kTab) {
+    int t0[kTab], t1[kTab], t2[kTab];
+#pragma unroll
+    for (int k = 0; k < kTab; ++k) {
+      const int p = p0 + k * 64 + lane;
+      if (p < np) {
+        const int32_t* q = plan + s.o_pieces + (int64_t)p * kPieceInts;
+        t0[k] = q[P_START]; t1[k] = q[P_CNT]; t2[k] = q[P_ROW0];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kTab; ++k) {
+      const int p = p0 + k * 64 + lane;
+      if (p < np) { pstart_s[p] = t0[k]; pcnt_s[p] = t1[k]; prow_s[p] = t2[k]; }
+    }
   }
-  // the wave's own counters are zeroed by the wave itself; LDS is in order per wave
+  // One wave: its LDS accesses are performed in program order, so no barrier is needed.
+  //
+  // Stable rank of each assignment among its expert's assignments, chunk by chunk (64
+  // assignments, lane order = i order): `below` = lanes of the chunk with the same id
+  // and a lower lane (ballot peer masks, one ballot per id bit); the group's lowest lane
+  // adds the group size to the expert's LDS counter and gets the count of all earlier
+  // chunks back (atomics of one wave are applied in issue order, so they are issued
+  // back to back without waiting), then hands it to its peers with a lane shuffle.
   const int nbits = 32 - __clz(E);
   const uint64_t lt = lanemask_lt();
-  int loc[M];
-  int32_t* myrun = run + wave * E;
+  for (int c0 = 0; c0 < M; c0 += kMapGroup) {
+    int below[kMapGroup], lead[kMapGroup], base[kMapGroup];
 #pragma unroll
-  for (int c = 0; c < M; ++c) {
-    const int id = idv[c];
-    uint64_t peers = ~0ull;
-    for (int bit = 0; bit < nbits; ++bit) {
-      const bool on = (id >> bit) & 1;
-      const uint64_t bl = __ballot(on);
-      peers &= on ? bl : ~bl;
-    }
-    const int below = __popcll(peers & lt);
-    int base = 0;
-    if (id < E) base = myrun[id];
-    loc[c] = base + below;
-    if (below == 0 && id < E) myrun[id] = base + __popcll(peers);
-  }
-  __syncthreads();
-
-  // per expert: block prefix (earlier blocks) + earlier waves of this block
-  for (int e = tid; e < E; e += kMapThreads) {
-    int acc = 0;
-    const int nb = blockIdx.x;
-    int b = 0;
-    for (; b + 4 <= nb; b += 4) {
-      const int c0 = ws[(int64_t)(b + 0) * E + e];
-      const int c1 = ws[(int64_t)(b + 1) * E + e];
-      const int c2 = ws[(int64_t)(b + 2) * E + e];
-      const int c3 = ws[(int64_t)(b + 3) * E + e];
-      acc += c0 + c1 + c2 + c3;
-    }
-    for (; b < nb; ++b) acc += ws[(int64_t)b * E + e];
-#pragma unroll
-    for (int v = 0; v < kMapWaves; ++v) {
-      const int c = run[v * E + e];
-      run[v * E + e] = acc;
-      acc += c;
-    }
-  }
-  __syncthreads();
-
-#pragma unroll
-  for (int c = 0; c < M; ++c) {
-    const int64_t i = i_wave + c * 64 + lane;
-    if (i < A) {
-      const int id = idv[c];
-      int row = -1;
-      if ((unsigned)id >= (unsigned)E) {
-        // cannot happen for ids the histogram saw; never index with it
-      } else if (const int j = myrun[id] + loc[c]; j < keep_s[id]) {
-        row = home_s[id] + j;
-      } else {
-        const int q1 = pfirst_s[id] + pnum_s[id];
-        for (int q = pfirst_s[id]; q < q1; ++q) {
-          const int st = pstart_s[q];
-          if (j < st + pcnt_s[q]) { row = prow_s[q] + (j - st); break; }
-        }
+    for (int u = 0; u < kMapGroup; ++u) {
+      const int id = idv[c0 + u];
+      uint64_t peers = ~0ull;
+      for (int bit = 0; bit < nbits; ++bit) {
+        const bool on = (id >> bit) & 1;
+        const uint64_t bl = __ballot(on);
+        peers &= on ? bl : ~bl;
       }
-      dst[i] = row;
-      wout[i] = wv[c];
+      below[u] = __popcll(peers & lt);
+      lead[u] = __builtin_ctzll(peers);
+      base[u] = 0;
+      if (below[u] == 0 && (unsigned)id < (unsigned)E)
+        base[u] = atomicAdd(&run[id], __popcll(peers));
+    }
+#pragma unroll
+    for (int u = 0; u < kMapGroup; ++u) {
+      const int c = c0 + u;
+      const int id = idv[c];
+      const int64_t i = i_wave + c * 64 + lane;
+      const int j = __shfl(base[u], lead[u], 64) + below[u];
+      if ((unsigned)id < (unsigned)E) {
+        int row = -1;
+        if (j < keep_s[id]) {
+          row = home_s[id] + j;
+        } else {
+          const int q1 = pfirst_s[id] + pnum_s[id];
+          for (int q = pfirst_s[id]; q < q1; ++q) {
+            const int st = pstart_s[q];
+            if (j < st + pcnt_s[q]) { row = prow_s[q] + (j - st); break; }
+          }
+        }
+        dst[i] = row;
+        wout[i] = wt[c];
+      }
     }
   }
 }
@@ -477,9 +632,16 @@ __global__ __launch_bounds__(kMapThreads) void map_kernel(const int32_t* __restr
 template <int M>
 hipError_t launch_map(const moonep_sizes& s, const int32_t* ids, const float* w, int32_t* plan,
                       const int32_t* ws, hipStream_t st) {
-  const size_t lds = (size_t)(kMapWaves * s.E + 4 * s.E + 3 * s.P_max) * sizeof(int32_t);
-  hipLaunchKernelGGL(map_kernel<M>, dim3(s.nblk), dim3(kMapThreads), lds, st, ids, w, plan,
+  const size_t lds = (size_t)(5 * s.E + 3 * s.P_max) * sizeof(int32_t);
+  hipLaunchKernelGGL(map_kernel<M>, dim3(s.nblk * kMapWaves), dim3(64), lds, st, ids, w, plan,
                      ws, s);
+  return hipGetLastError();
+}
+
+template <int M>
+hipError_t launch_hist(const moonep_sizes& s, const int32_t* ids, int32_t* ws, hipStream_t st) {
+  hipLaunchKernelGGL(hist_kernel<M>, dim3(s.nblk), dim3(kMapThreads),
+                     (size_t)kMapWaves * s.E * sizeof(int32_t), st, ids, ws, s);
   return hipGetLastError();
 }
 
@@ -487,12 +649,19 @@ hipError_t launch_map(const moonep_sizes& s, const int32_t* ids, const float* w,
 
 hipError_t launch_plan(const moonep_sizes& s, const int32_t* ids, const float* w,
                        int32_t* plan, int32_t* ws, hipStream_t st) {
-  hipLaunchKernelGGL(hist_kernel, dim3(s.nblk), dim3(kMapThreads),
-                     (size_t)s.E * sizeof(int32_t), st, ids, ws, s);
-  hipError_t err = hipGetLastError();
+  hipError_t err;
+  switch (s.blk / kMapThreads) {
+    case 1: err = launch_hist<1>(s, ids, ws, st); break;
+    case 2: err = launch_hist<2>(s, ids, ws, st); break;
+    case 4: err = launch_hist<4>(s, ids, ws, st); break;
+    case 8: err = launch_hist<8>(s, ids, ws, st); break;
+    case 16: err = launch_hist<16>(s, ids, ws, st); break;
+    case 32: err = launch_hist<32>(s, ids, ws, st); break;
+    default: return hipErrorInvalidValue;
+  }
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(planner_kernel, dim3(1), dim3(kPlanThreads),
-                     (size_t)6 * s.E * sizeof(int32_t), st, plan, ws, s);
+  const size_t plds = (size_t)(7 * s.E + max(kPlanThreads, 7 * s.P_max)) * sizeof(int32_t);
+  hipLaunchKernelGGL(planner_kernel, dim3(1), dim3(kPlanThreads), plds, st, plan, ws, s);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   switch (s.blk / kMapThreads) {
