@@ -68,6 +68,8 @@ inline int fill_sizes(int R, int E, int K, int S, int slots, moonep_sizes* s) {
   s->o_slot_expert = o; o += align64((int64_t)R * (slots > 0 ? slots : 1));
   s->o_off = o;         o += align64((int64_t)R * (G + 1));
   s->o_red = o;         o += align64(E);
+  s->o_xtab = o;        o += align64((int64_t)4 * E);            // int4 per expert
+  s->o_ptab = o;        o += align64((int64_t)4 * s->P_max);     // int4 per piece
   s->o_dst_row = o;     o += align64(A);
   s->o_w = o;           o += align64(A);
   s->plan_bytes = o * 4;

@@ -28,6 +28,8 @@
 namespace moonep {
 namespace {
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int l = __lane_id();
   return l == 0 ? 0ull : (~0ull >> (64 - l));
@@ -138,6 +140,7 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
   int32_t* pst_s = pc_s + PM;
   int32_t* pfb_s = pst_s + PM;
   int32_t* prow_s = pfb_s + PM;
+  int32_t* home_s = list_s;         // [E] home group rows, after the ordering is done
   int32_t* part_s = pe_s;           // [kPlanThreads] column segment sums, used before the
                                     // pieces exist
   __shared__ int32_t hl_s[64], used_s[64], fb_s[64], nfb_s[64];
@@ -363,7 +366,7 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
       const int incl = wave_incl_scan(a);
       if (g < E_loc) {
         o[g] = carry + incl - a;
-        plan[s.o_home_row + r * E_loc + g] = r * NvS + carry + incl - a;
+        home_s[r * E_loc + g] = r * NvS + carry + incl - a;
       }
       carry += lane63(incl);
     }
@@ -401,12 +404,20 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
     pc[P_E] = pe_s[p]; pc[P_R] = pr_s[p]; pc[P_SLOT] = psl_s[p]; pc[P_CNT] = pc_s[p];
     pc[P_START] = pst_s[p]; pc[P_FBPOS] = pfb_s[p]; pc[P_ROW0] = prow_s[p]; pc[7] = 0;
   }
+  for (int p = tid; p < np; p += kPlanThreads) {
+    // packed (start, count, first row) for the map kernel
+    reinterpret_cast<i32x4*>(plan + s.o_ptab)[p] = i32x4{pst_s[p], pc_s[p], prow_s[p], 0};
+  }
   for (int e = tid; e < E; e += kPlanThreads) {
     plan[s.o_load + e] = load_s[e];
     plan[s.o_shed + e] = shed_s[e];
     plan[s.o_keep + e] = keep_s[e];
+    plan[s.o_home_row + e] = home_s[e];
     plan[s.o_pfirst + e] = pfirst_s[e];
     plan[s.o_pnum + e] = pnum_s[e];
+    // packed (keep, home row, first piece, piece count) for the map kernel
+    reinterpret_cast<i32x4*>(plan + s.o_xtab)[e] =
+        i32x4{keep_s[e], home_s[e], pfirst_s[e], pnum_s[e]};
   }
   if (col_thread) {
     // per-block bases for the map kernel
@@ -500,17 +511,12 @@ __global__ __launch_bounds__(64) void map_kernel(const int32_t* __restrict__ ids
                                                  int32_t* __restrict__ plan,
                                                  const int32_t* __restrict__ ws,
                                                  const moonep_sizes s) {
-  extern __shared__ int32_t lds[];
+  extern __shared__ i32x4 lds4[];
   const int E = s.E;
   const int P = s.P_max;
-  int32_t* run = lds;                  // [E]  assignments of e before the current chunk
-  int32_t* keep_s = run + E;           // [E]
-  int32_t* home_s = keep_s + E;        // [E]
-  int32_t* pfirst_s = home_s + E;      // [E]
-  int32_t* pnum_s = pfirst_s + E;      // [E]
-  int32_t* pstart_s = pnum_s + E;      // [P]
-  int32_t* pcnt_s = pstart_s + P;      // [P]
-  int32_t* prow_s = pcnt_s + P;        // [P]
+  i32x4* xtab_s = lds4;                            // [E] keep, home row, first piece, count
+  i32x4* ptab_s = xtab_s + E;                      // [P] start, count, first row
+  int32_t* run = reinterpret_cast<int32_t*>(ptab_s + P);   // [E] running count per expert
 
   constexpr int kMapGroup = MapGroup<M>::value;   // chunks ranked per pass
   const int lane = threadIdx.x;
@@ -521,6 +527,8 @@ __global__ __launch_bounds__(64) void map_kernel(const int32_t* __restrict__ ids
   float* wout = reinterpret_cast<float*>(plan + s.o_w);
   if (i_wave >= A) return;
 
+  // every load is issued before the first wait: status, ids, weights, expert tables and
+  // this sub-block's bases, piece table (P_max entries, whatever the piece count)
   const int status = plan[s.o_hdr + H_STATUS];
   int idv[M];
   float wt[M];
@@ -530,6 +538,31 @@ __global__ __launch_bounds__(64) void map_kernel(const int32_t* __restrict__ ids
     idv[c] = i < A ? ids[i] : E;    // E marks lanes past the end
     wt[c] = i < A ? w[i] : 0.f;
   }
+  const i32x4* xtab = reinterpret_cast<const i32x4*>(plan + s.o_xtab);
+  const i32x4* ptab = reinterpret_cast<const i32x4*>(plan + s.o_ptab);
+  const int32_t* bbase = ws + (int64_t)b * E;
+  const int32_t* wbase = ws + ws_sub(s) + ((int64_t)b * kMapWaves + sw) * E;
+  // loads use clamped (always valid) indices so that they stay unconditional and the
+  // values stay in registers; only the LDS stores are guarded
+  for (int e0 = 0; e0 < E || e0 < P; e0 += 64 * kTab) {
+    i32x4 xt[kTab], pt[kTab];
+    int bb[kTab], wb[kTab];
+#pragma unroll
+    for (int k = 0; k < kTab; ++k) {
+      const int e = e0 + k * 64 + lane;
+      const int ec = min(e, E - 1), pc = min(e, P - 1);
+      xt[k] = xtab[ec];
+      bb[k] = bbase[ec];
+      wb[k] = wbase[ec];
+      pt[k] = ptab[pc];
+    }
+#pragma unroll
+    for (int k = 0; k < kTab; ++k) {
+      const int e = e0 + k * 64 + lane;
+      if (e < E) { xtab_s[e] = xt[k]; run[e] = bb[k] + wb[k]; }
+      if (e < P) ptab_s[e] = pt[k];
+    }
+  }
   if (status != 0) {
     // invalid plan: map nothing
 #pragma unroll
@@ -538,45 +571,6 @@ __global__ __launch_bounds__(64) void map_kernel(const int32_t* __restrict__ ids
       if (i < A) { dst[i] = -1; wout[i] = 0.f; }
     }
     return;
-  }
-  // tables to LDS, kTab entries per lane per round trip (loads first, then stores)
-  const int32_t* bbase = ws + (int64_t)b * E;
-  const int32_t* wbase = ws + ws_sub(s) + ((int64_t)b * kMapWaves + sw) * E;
-  for (int e0 = 0; e0 < E; e0 += 64 * kTab) {
-    int t0[kTab], t1[kTab], t2[kTab], t3[kTab], t4[kTab], t5[kTab];
-#pragma unroll
-    for (int k = 0; k < kTab; ++k) {
-      const int e = e0 + k * 64 + lane;
-      if (e < E) {
-        t0[k] = bbase[e]; t1[k] = wbase[e]; t2[k] = plan[s.o_keep + e];
-        t3[k] = plan[s.o_home_row + e]; t4[k] = plan[s.o_pfirst + e]; t5[k] = plan[s.o_pnum + e];
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kTab; ++k) {
-      const int e = e0 + k * 64 + lane;
-      if (e < E) {
-        run[e] = t0[k] + t1[k]; keep_s[e] = t2[k]; home_s[e] = t3[k];
-        pfirst_s[e] = t4[k]; pnum_s[e] = t5[k];
-      }
-    }
-  }
-  const int np = plan[s.o_hdr + H_NPIECES];
-  for (int p0 = 0; p0 < np; p0 += 64 * kTab) {
-    int t0[kTab], t1[kTab], t2[kTab];
-#pragma unroll
-    for (int k = 0; k < kTab; ++k) {
-      const int p = p0 + k * 64 + lane;
-      if (p < np) {
-        const int32_t* q = plan + s.o_pieces + (int64_t)p * kPieceInts;
-        t0[k] = q[P_START]; t1[k] = q[P_CNT]; t2[k] = q[P_ROW0];
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kTab; ++k) {
-      const int p = p0 + k * 64 + lane;
-      if (p < np) { pstart_s[p] = t0[k]; pcnt_s[p] = t1[k]; prow_s[p] = t2[k]; }
-    }
   }
   // One wave: its LDS accesses are performed in program order, so no barrier is needed.
   //
@@ -589,37 +583,47 @@ __global__ __launch_bounds__(64) void map_kernel(const int32_t* __restrict__ ids
   const int nbits = 32 - __clz(E);
   const uint64_t lt = lanemask_lt();
   for (int c0 = 0; c0 < M; c0 += kMapGroup) {
-    int below[kMapGroup], lead[kMapGroup], base[kMapGroup];
+    // peer masks of kMapGroup chunks at once (independent chains, one ballot per id bit)
+    uint64_t peers[kMapGroup];
+#pragma unroll
+    for (int u = 0; u < kMapGroup; ++u) peers[u] = ~0ull;
+    for (int bit = 0; bit < nbits; ++bit) {
+#pragma unroll
+      for (int u = 0; u < kMapGroup; ++u) {
+        const bool on = (idv[c0 + u] >> bit) & 1;
+        const uint64_t bl = __ballot(on);
+        peers[u] &= on ? bl : ~bl;
+      }
+    }
+    int below[kMapGroup], base[kMapGroup];
 #pragma unroll
     for (int u = 0; u < kMapGroup; ++u) {
       const int id = idv[c0 + u];
-      uint64_t peers = ~0ull;
-      for (int bit = 0; bit < nbits; ++bit) {
-        const bool on = (id >> bit) & 1;
-        const uint64_t bl = __ballot(on);
-        peers &= on ? bl : ~bl;
-      }
-      below[u] = __popcll(peers & lt);
-      lead[u] = __builtin_ctzll(peers);
+      below[u] = __popcll(peers[u] & lt);
       base[u] = 0;
       if (below[u] == 0 && (unsigned)id < (unsigned)E)
-        base[u] = atomicAdd(&run[id], __popcll(peers));
+        base[u] = atomicAdd(&run[id], __popcll(peers[u]));
+    }
+    int j[kMapGroup];
+    i32x4 xt[kMapGroup];
+#pragma unroll
+    for (int u = 0; u < kMapGroup; ++u) {
+      j[u] = __shfl(base[u], __builtin_ctzll(peers[u]), 64) + below[u];
+      xt[u] = xtab_s[min((unsigned)idv[c0 + u], (unsigned)(E - 1))];   // keep, home row, pieces
     }
 #pragma unroll
     for (int u = 0; u < kMapGroup; ++u) {
       const int c = c0 + u;
       const int id = idv[c];
       const int64_t i = i_wave + c * 64 + lane;
-      const int j = __shfl(base[u], lead[u], 64) + below[u];
       if ((unsigned)id < (unsigned)E) {
         int row = -1;
-        if (j < keep_s[id]) {
-          row = home_s[id] + j;
+        if (j[u] < xt[u].x) {
+          row = xt[u].y + j[u];
         } else {
-          const int q1 = pfirst_s[id] + pnum_s[id];
-          for (int q = pfirst_s[id]; q < q1; ++q) {
-            const int st = pstart_s[q];
-            if (j < st + pcnt_s[q]) { row = prow_s[q] + (j - st); break; }
+          for (int q = xt[u].z; q < xt[u].z + xt[u].w; ++q) {
+            const i32x4 pt = ptab_s[q];      // start, count, first row
+            if (j[u] < pt.x + pt.y) { row = pt.z + (j[u] - pt.x); break; }
           }
         }
         dst[i] = row;
@@ -632,7 +636,7 @@ __global__ __launch_bounds__(64) void map_kernel(const int32_t* __restrict__ ids
 template <int M>
 hipError_t launch_map(const moonep_sizes& s, const int32_t* ids, const float* w, int32_t* plan,
                       const int32_t* ws, hipStream_t st) {
-  const size_t lds = (size_t)(5 * s.E + 3 * s.P_max) * sizeof(int32_t);
+  const size_t lds = (size_t)(5 * s.E + 4 * s.P_max) * sizeof(int32_t);
   hipLaunchKernelGGL(map_kernel<M>, dim3(s.nblk * kMapWaves), dim3(64), lds, st, ids, w, plan,
                      ws, s);
   return hipGetLastError();

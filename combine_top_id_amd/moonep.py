@@ -29,8 +29,8 @@ class Sizes(ctypes.Structure):
                [(n, ctypes.c_int32) for n in ("nblk", "blk")] + \
                [(n, ctypes.c_int64) for n in ("o_hdr", "o_load", "o_shed", "o_keep",
                                               "o_home_row", "o_pfirst", "o_pnum", "o_pieces",
-                                              "o_slot_expert", "o_off", "o_red", "o_dst_row",
-                                              "o_w")]
+                                              "o_slot_expert", "o_off", "o_red", "o_xtab",
+                                              "o_ptab", "o_dst_row", "o_w")]
 
 
 class PlanDesc(ctypes.Structure):

@@ -65,7 +65,7 @@ typedef struct moonep_sizes {
   int32_t nblk, blk;        /* assignment blocks used by the plan kernels                */
   /* int32-element offsets of the plan blob's arrays (for inspection and tests):        */
   int64_t o_hdr, o_load, o_shed, o_keep, o_home_row, o_pfirst, o_pnum, o_pieces,
-          o_slot_expert, o_off, o_red, o_dst_row, o_w;
+          o_slot_expert, o_off, o_red, o_xtab, o_ptab, o_dst_row, o_w;
 } moonep_sizes;
 
 /* Host-side handle of a plan: sizes plus the caller's device blob.  Filled by
