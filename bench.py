@@ -99,8 +99,15 @@ def cpu_baseline(wl, ids_np, w_np, x_np, budget_s=15.0):
     probe = min(1024, wl.T)
     td, tc = run(probe)
     n = int(min(wl.T, max(probe, probe * budget_s / max(td + tc, 1e-6))))
+    reps = 1
     if n > probe:
         td, tc = run(n)
+    if n == wl.T and td + tc < budget_s / 2:
+        # the whole batch is shorter than the budget: repeat it, keep the median
+        runs = [(td, tc)] + [run(n) for _ in range(2)]
+        runs.sort(key=lambda r: r[0] + r[1])
+        td, tc = runs[1]
+        reps = 3
     nbytes = dispatch_bytes(n, wl.K, wl.H) + combine_bytes(n, wl.K, wl.H)
     return {
         "value": round(nbytes / (td + tc) / 1e9, 4),
@@ -109,7 +116,7 @@ def cpu_baseline(wl, ids_np, w_np, x_np, budget_s=15.0):
         "kind": "oracle",
         "sample": f"oracle plan+slot map on the full maxvio={wl.maxvio[0]} batch "
                   f"({t_plan * 1e3:.1f} ms), then dispatch+combine of its first {n} of "
-                  f"{wl.T} tokens ({td:.2f} s + {tc:.2f} s); numpy, 1 thread",
+                  f"{wl.T} tokens ({td:.2f} s + {tc:.2f} s, median of {reps}); numpy, 1 thread",
         "plan_ms": round(t_plan * 1e3, 2),
         "host_cpus": len(os.sched_getaffinity(0)),
     }
