@@ -331,3 +331,37 @@ def reduce_grad(p: Plan, home_grad, rep_grad):
         if slot >= 0:
             home[e] = (home[e] + rep[r, slot]).astype(np.float32)
     return home
+
+
+# ----------------------------------------------------------------------------------------
+# backward pair, reusing the plan ([dive, section 4, design pattern 1]: the plan computed
+# in forward serves both backward passes)
+# ----------------------------------------------------------------------------------------
+
+def dispatch_bwd(dst_row, g_recv_bits):
+    """Gradient of dispatch with respect to x: dispatch copied x[t] into K rows, so
+    gx[t] = bf16( sum_k g_recv[dst_row[t, k]] ), summed in fp32, k ascending."""
+    dst_row = np.asarray(dst_row)
+    T, K = dst_row.shape
+    acc = np.zeros((T, g_recv_bits.shape[1]), dtype=np.float32)
+    for k in range(K):
+        acc = (acc + bf16_to_f32(g_recv_bits[dst_row[:, k]])).astype(np.float32)
+    return f32_to_bf16_rne(acc)
+
+
+def combine_bwd(dst_row, w, dout_bits, y_bits, total_rows):
+    """Gradient of combine out[t] = sum_k w[t,k] * y[dst_row[t,k]]:
+      g_y[dst_row[t,k]] = bf16( w[t,k] * dout[t] )   (fp32 product, then bf16 RNE)
+      dw[t, k]          = sum_h dout[t,h] * y[dst_row[t,k], h]   (float64 here)
+    Rows of g_y no assignment maps to stay zero."""
+    dst_row = np.asarray(dst_row)
+    w = np.asarray(w, dtype=np.float32)
+    T, K = dst_row.shape
+    d32 = bf16_to_f32(dout_bits)
+    g_y = np.zeros((total_rows, dout_bits.shape[1]), dtype=np.uint16)
+    dw = np.zeros((T, K), dtype=np.float64)
+    for k in range(K):
+        g_y[dst_row[:, k]] = f32_to_bf16_rne((w[:, k:k + 1] * d32).astype(np.float32))
+        yk = bf16_to_f32(y_bits[dst_row[:, k]]).astype(np.float64)
+        dw[:, k] = (d32.astype(np.float64) * yk).sum(axis=1)
+    return g_y, dw

@@ -483,3 +483,73 @@ def test_workload_plans(wl, mi):
     if wl.slots == wl.E // wl.R:
         # training budget E/R: these routings need no fallback
         assert p.n_fallback == 0
+
+
+# ----------------------------------------------------------------------------------------
+# backward pair
+# ----------------------------------------------------------------------------------------
+
+def _bwd_case(seed=20260102):
+    w, ids, wt, x = _tiny_inputs(seed=seed)
+    p = O.plan(ids, w.R, w.E, w.K, w.S, w.slots)
+    dst = O.slot_map(p, ids)
+    rows = w.R * p.sz.NvS
+    rng = np.random.default_rng(seed)
+    g_recv = O.f32_to_bf16_rne(rng.standard_normal((rows, w.H)).astype(np.float32))
+    dout = O.f32_to_bf16_rne(rng.standard_normal((w.T, w.H)).astype(np.float32))
+    y = O.f32_to_bf16_rne(rng.standard_normal((rows, w.H)).astype(np.float32))
+    return w, ids, wt, x, p, dst, rows, g_recv, dout, y
+
+
+def test_dispatch_bwd_is_the_adjoint_of_dispatch():
+    """<dispatch(x), g> == <x, dispatch_bwd(g)> over the mapped rows (float64; the
+    bf16 rounding of gx is undone by comparing against the fp32 sums' tolerance)."""
+    w, ids, wt, x, p, dst, rows, g_recv, dout, y = _bwd_case()
+    recv = O.dispatch(dst, x, rows)
+    mapped = np.zeros(rows, dtype=bool)
+    mapped[dst.reshape(-1)] = True
+    lhs = (O.bf16_to_f32(recv[mapped]).astype(np.float64) *
+           O.bf16_to_f32(g_recv[mapped]).astype(np.float64)).sum()
+    gx = O.dispatch_bwd(dst, g_recv)
+    rhs = (O.bf16_to_f32(x).astype(np.float64) * O.bf16_to_f32(gx).astype(np.float64)).sum()
+    # gx is rounded to bf16: bound the rounding by 2^-8 relative per element
+    bound = (np.abs(O.bf16_to_f32(x)).astype(np.float64) *
+             np.abs(O.bf16_to_f32(gx)).astype(np.float64)).sum() * 2.0 ** -8
+    assert abs(lhs - rhs) <= bound
+    # and exactly: gx[t] is the rounded fp32 sum of the K gradient rows of token t
+    for t in range(0, w.T, 7):
+        acc = np.zeros(w.H, dtype=np.float32)
+        for k in range(w.K):
+            acc = (acc + O.bf16_to_f32(g_recv[dst[t, k]])).astype(np.float32)
+        assert (gx[t] == O.f32_to_bf16_rne(acc)).all()
+
+
+def test_combine_bwd_matches_float64_autograd():
+    """Autograd of the plan-free combine out[t] = sum_k w[t,k] * y_{t,k} in float64."""
+    w, ids, wt, x, p, dst, rows, g_recv, dout, y = _bwd_case(20260103)
+    g_y, dw = O.combine_bwd(dst, wt, dout, y, rows)
+    yk = torch.tensor(O.bf16_to_f32(y[dst]).astype(np.float64), requires_grad=True)   # [T,K,H]
+    wk = torch.tensor(wt.astype(np.float64), requires_grad=True)                         # [T,K]
+    out = (wk[:, :, None] * yk).sum(1)
+    out.backward(torch.tensor(O.bf16_to_f32(dout).astype(np.float64)))
+    assert_close(dw, wk.grad.numpy(), RTOL_FP32)
+    # g_y rows are the rounded per-assignment gradients w * dout
+    ref = yk.grad.numpy()                                                                # [T,K,H]
+    assert_close(O.bf16_to_f32(g_y[dst]), ref, 2.0 ** -8)
+    exact = O.f32_to_bf16_rne((wt[:, :, None] * O.bf16_to_f32(dout)[:, None, :]).astype(np.float32))
+    assert (g_y[dst] == exact).all()
+
+
+def test_backward_round_trip_closed_form():
+    """combine_bwd then dispatch_bwd gives sum_k bf16(w[t,k] dout[t]) for each token: the
+    gradient of x through dispatch -> identity expert -> combine."""
+    w, ids, wt, x, p, dst, rows, g_recv, dout, y = _bwd_case(20260104)
+    g_y, dw = O.combine_bwd(dst, wt, dout, y, rows)
+    gx = O.dispatch_bwd(dst, g_y)
+    d32 = O.bf16_to_f32(dout)
+    acc = np.zeros_like(d32)
+    for k in range(w.K):
+        acc = (acc + O.bf16_to_f32(O.f32_to_bf16_rne((wt[:, k:k + 1] * d32).astype(np.float32)))).astype(np.float32)
+    assert (gx == O.f32_to_bf16_rne(acc)).all()
+    # weights sum to one, so this is dout up to bf16 rounding of the K pieces
+    assert_close(O.bf16_to_f32(gx), d32, 2 * 2.0 ** -8)
