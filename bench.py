@@ -129,6 +129,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--flush", choices=("auto", "on", "off"), default="auto",
                     help="write a 1 GiB buffer before every step so no input is served from "
                          "the 256 MB last-level cache (auto: when a step moves < 2 GB)")
@@ -251,6 +252,39 @@ def main():
     achieved = dom_bytes / dom_us / 1e3
     dc_times = [r["dispatch_us"] + r["combine_us"] for r in rows]
 
+    # backward pair on the first batch, reusing its plan: dispatch-bwd of a gradient laid
+    # out like recv, combine-bwd of a gradient laid out like out (y = recv)
+    backward = None
+    if not args.no_backward:
+        b0 = batches[0]
+        plan = M.moonep_plan(b0["ids"], b0["w"], wl.R, wl.E, wl.K, wl.S, wl.slots, plan=plan)
+        M.moonep_dispatch(plan, b0["x"], recv)
+        g_y = torch.empty_like(recv)
+        dw = torch.empty(wl.T, wl.K, dtype=torch.float32, device=dev)
+        gx = torch.empty_like(out)
+        dout = b0["x"]                       # any bf16 [T, H] gradient
+        reps = 10
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        M.moonep_combine_bwd(plan, dout, recv, g_y, dw)
+        M.moonep_dispatch_bwd(plan, g_y, gx)
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for _ in range(reps):
+            M.moonep_combine_bwd(plan, dout, recv, g_y, dw)
+        ev[1].record(stream)
+        for _ in range(reps):
+            M.moonep_dispatch_bwd(plan, g_y, gx)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        tcb = ev[0].elapsed_time(ev[1]) * 1e3 / reps
+        tdb = ev[1].elapsed_time(ev[2]) * 1e3 / reps
+        cbb = wl.T * (2 * wl.K + 1) * 2 * wl.H + wl.T * 12 * wl.K
+        dbb = dispatch_bytes(wl.T, wl.K, wl.H)
+        backward = dict(combine_bwd_us=round(tcb, 2), combine_bwd_gbps=round(cbb / tcb / 1e3, 1),
+                        dispatch_bwd_us=round(tdb, 2), dispatch_bwd_gbps=round(dbb / tdb / 1e3, 1),
+                        bytes_per_token="combine_bwd (2K+1)*2H + 12K; dispatch_bwd (K+1)*2H + 4K")
+        del g_y, dw, gx
+
     # a plain device copy of 4 GiB as a measured ceiling on the same box
     a = torch.empty(1 << 31, dtype=torch.int16, device=dev)
     c = torch.empty_like(a)
@@ -304,6 +338,7 @@ def main():
         "flatness_max_over_min": round(max(dc_times) / min(dc_times), 4),
         "plan_us_median": round(statistics.median([r["plan_us"] for r in rows]), 2),
         "copy_ceiling_gbps": round(copy_gbps, 1),
+        "backward": backward,
     }
     if not args.no_cpu_baseline:
         b0 = batches[0]

@@ -3,5 +3,5 @@ weighted combine -> replica-gradient reduce, as HIP kernels behind a C ABI
 (include/moonep.h, libmoonep.so), with a thin ctypes binding."""
 
 from .moonep import (moonep_query, moonep_plan, moonep_dispatch, moonep_combine,  # noqa: F401
-                     moonep_reduce_grad, moonep_plan_status, Plan, Sizes, MoonepError, lib,
-                     LIB_PATH, EXPORTS)
+                     moonep_reduce_grad, moonep_plan_status, moonep_dispatch_bwd,
+                     moonep_combine_bwd, Plan, Sizes, MoonepError, lib, LIB_PATH, EXPORTS)

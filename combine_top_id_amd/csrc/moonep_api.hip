@@ -73,6 +73,29 @@ int moonep_combine(const moonep_plan_desc* plan, const uint16_t* y, int H, uint1
   return err == hipSuccess ? MOONEP_OK : MOONEP_EHIP;
 }
 
+int moonep_dispatch_bwd(const moonep_plan_desc* plan, const uint16_t* g_recv, int H,
+                        uint16_t* gx, hipStream_t stream) {
+  const int rc = check_desc(plan);
+  if (rc != MOONEP_OK) return rc;
+  if (!g_recv || !gx || H <= 0 || H % 8 != 0) return MOONEP_EINVAL;
+  if (!aligned(g_recv, 16) || !aligned(gx, 16)) return MOONEP_EALIGN;
+  const hipError_t err = launch_dispatch_bwd(plan->sz, static_cast<const int32_t*>(plan->dev),
+                                             g_recv, H, gx, stream);
+  return err == hipSuccess ? MOONEP_OK : MOONEP_EHIP;
+}
+
+int moonep_combine_bwd(const moonep_plan_desc* plan, const uint16_t* dout, const uint16_t* y,
+                       int H, uint16_t* g_y, float* dw, hipStream_t stream) {
+  const int rc = check_desc(plan);
+  if (rc != MOONEP_OK) return rc;
+  if (!dout || !y || !g_y || !dw || H <= 0 || H % 8 != 0) return MOONEP_EINVAL;
+  if (!aligned(dout, 16) || !aligned(y, 16) || !aligned(g_y, 16) || !aligned(dw, 4))
+    return MOONEP_EALIGN;
+  const hipError_t err = launch_combine_bwd(plan->sz, static_cast<const int32_t*>(plan->dev),
+                                            dout, y, H, g_y, dw, stream);
+  return err == hipSuccess ? MOONEP_OK : MOONEP_EHIP;
+}
+
 int moonep_reduce_grad(const moonep_plan_desc* plan, float* home_grad, const float* rep_grad,
                        int64_t G_el, hipStream_t stream) {
   const int rc = check_desc(plan);

@@ -92,6 +92,11 @@ hipError_t launch_dispatch(const moonep_sizes& s, const int32_t* plan, const uin
                            int H, uint16_t* recv, hipStream_t st);
 hipError_t launch_combine(const moonep_sizes& s, const int32_t* plan, const uint16_t* y,
                           int H, uint16_t* out, hipStream_t st);
+hipError_t launch_dispatch_bwd(const moonep_sizes& s, const int32_t* plan, const uint16_t* g_recv,
+                               int H, uint16_t* gx, hipStream_t st);
+hipError_t launch_combine_bwd(const moonep_sizes& s, const int32_t* plan, const uint16_t* dout,
+                              const uint16_t* y, int H, uint16_t* g_y, float* dw,
+                              hipStream_t st);
 hipError_t launch_reduce(const moonep_sizes& s, const int32_t* plan, float* home,
                          const float* rep, int64_t G_el, hipStream_t st);
 

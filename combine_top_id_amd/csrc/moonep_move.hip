@@ -65,7 +65,7 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t* __restric
 // ---------------------------------------------------------------------------------------
 // acc += w * y[row, v0 + u*blockDim.x] for the thread's U vectors (8 bf16 each): a
 // separate fp32 multiply and add per element, in the caller's k order.
-template <int U>
+template <int U, bool WEIGHTED>
 __device__ __forceinline__ void combine_accumulate(float (&acc)[U][8], const u32x4* __restrict__ y,
                                                    int row, float wk, int v0, int nvec,
                                                    int nrows) {
@@ -82,15 +82,16 @@ __device__ __forceinline__ void combine_accumulate(float (&acc)[U][8], const u32
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const unsigned int bits = yv[u][q];
-      const float p0 = wk * bf_lo(bits);
-      const float p1 = wk * bf_hi(bits);
+      const float p0 = WEIGHTED ? wk * bf_lo(bits) : bf_lo(bits);
+      const float p1 = WEIGHTED ? wk * bf_hi(bits) : bf_hi(bits);
       acc[u][2 * q] = acc[u][2 * q] + p0;
       acc[u][2 * q + 1] = acc[u][2 * q + 1] + p1;
     }
   }
 }
 
-template <int KT, int U>
+// WEIGHTED = false is the gradient of dispatch: gx[t] = bf16(sum_k g_recv[dst_row[t,k]]).
+template <int KT, int U, bool WEIGHTED>
 __global__ __launch_bounds__(1024) void combine_kernel(const int32_t* __restrict__ dst,
                                                       const float* __restrict__ wts,
                                                       const u32x4* __restrict__ y,
@@ -110,10 +111,10 @@ __global__ __launch_bounds__(1024) void combine_kernel(const int32_t* __restrict
     if constexpr (KT > 0) {
 #pragma unroll
       for (int k = 0; k < KT; ++k)
-        combine_accumulate<U>(acc, y, d[k], wt[k], v0, nvec, nrows);
+        combine_accumulate<U, WEIGHTED>(acc, y, d[k], WEIGHTED ? wt[k] : 1.f, v0, nvec, nrows);
     } else {
       for (int k = 0; k < K; ++k)
-        combine_accumulate<U>(acc, y, d[k], wt[k], v0, nvec, nrows);
+        combine_accumulate<U, WEIGHTED>(acc, y, d[k], WEIGHTED ? wt[k] : 1.f, v0, nvec, nrows);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -126,6 +127,102 @@ __global__ __launch_bounds__(1024) void combine_kernel(const int32_t* __restrict
         __builtin_nontemporal_store(o, out + t * nvec + v);
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// combine backward: g_y[dst_row[t,k]] = bf16(w[t,k] * dout[t]);
+//                   dw[t,k] = sum_h dout[t,h] * y[dst_row[t,k],h]   (fp32, fused multiply-add)
+// ---------------------------------------------------------------------------------------
+// One workgroup per token.  Each thread holds U vectors of dout, reads the same vectors of
+// each of the K rows of y, keeps K partial dot products, and writes the scaled dout
+// vectors to the K rows of g_y (g_y may be y itself: each element is read before it is
+// written by the same thread).  The K partials are summed over the wave with lane
+// shuffles, then over the waves in LDS.  KMAX = K when K is a compile-time
+// constant, else MOONEP_MAX_K with the loop bounded by the runtime K.
+template <int KMAX, int U>
+__global__ __launch_bounds__(1024) void combine_bwd_kernel(const int32_t* __restrict__ dst,
+                                                           const float* __restrict__ wts,
+                                                           const u32x4* __restrict__ dout,
+                                                           const u32x4* y, u32x4* g_y,
+                                                           float* __restrict__ dw, int K,
+                                                           int nvec, int nrows) {
+  __shared__ float red[16][KMAX];
+  const int64_t t = blockIdx.x;
+  const int32_t* d = dst + t * K;
+  const float* wt = wts + t * K;
+  float part[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) part[k] = 0.f;
+  for (int v0 = threadIdx.x; v0 < nvec; v0 += blockDim.x * U) {
+    u32x4 dv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int v = v0 + u * blockDim.x;
+      dv[u] = v < nvec ? __builtin_nontemporal_load(dout + t * nvec + v) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      if (k >= K) break;
+      const int row = d[k];
+      if ((unsigned)row >= (unsigned)nrows) continue;     // -1: unmapped
+      const float wk = wt[k];
+      const u32x4* ysrc = y + (int64_t)row * nvec;
+      u32x4* gdst = g_y + (int64_t)row * nvec;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + u * blockDim.x;
+        if (v < nvec) {
+          const u32x4 yv = __builtin_nontemporal_load(ysrc + v);
+          u32x4 g;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float d0 = bf_lo(dv[u][q]), d1 = bf_hi(dv[u][q]);
+            part[k] = __builtin_fmaf(d0, bf_lo(yv[q]), part[k]);
+            part[k] = __builtin_fmaf(d1, bf_hi(yv[q]), part[k]);
+            const float g0 = wk * d0;
+            const float g1 = wk * d1;
+            g[q] = to_bf16(g0) | (to_bf16(g1) << 16);
+          }
+          __builtin_nontemporal_store(g, gdst + v);
+        }
+      }
+    }
+  }
+  // sum the partial dot products over the workgroup
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    if (k >= K) break;
+    float v = part[k];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (lane == 0) red[wave][k] = v;
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < K) {
+    const int k = threadIdx.x;
+    float v = 0.f;
+    const int nw = (blockDim.x + 63) >> 6;
+    for (int w = 0; w < nw; ++w) v += red[w][k];
+    dw[t * K + k] = d[k] >= 0 ? v : 0.f;
+  }
+}
+
+template <int KMAX>
+void launch_combine_bwd_k(const moonep_sizes& s, const int32_t* dst, const float* w,
+                          const uint16_t* dout, const uint16_t* y, uint16_t* g_y, float* dw,
+                          int nvec, int threads, int u, hipStream_t st) {
+  const dim3 grid((unsigned)s.T), block(threads);
+  const u32x4* dv = reinterpret_cast<const u32x4*>(dout);
+  const u32x4* yv = reinterpret_cast<const u32x4*>(y);
+  u32x4* gv = reinterpret_cast<u32x4*>(g_y);
+  const int nrows = (int)s.recv_rows;
+  switch (u) {
+    case 1: hipLaunchKernelGGL((combine_bwd_kernel<KMAX, 1>), grid, block, 0, st, dst, w, dv, yv, gv, dw, s.K, nvec, nrows); break;
+    case 2: hipLaunchKernelGGL((combine_bwd_kernel<KMAX, 2>), grid, block, 0, st, dst, w, dv, yv, gv, dw, s.K, nvec, nrows); break;
+    case 3: hipLaunchKernelGGL((combine_bwd_kernel<KMAX, 3>), grid, block, 0, st, dst, w, dv, yv, gv, dw, s.K, nvec, nrows); break;
+    default: hipLaunchKernelGGL((combine_bwd_kernel<KMAX, 4>), grid, block, 0, st, dst, w, dv, yv, gv, dw, s.K, nvec, nrows); break;
   }
 }
 
@@ -206,23 +303,23 @@ void launch_dispatch_u(const moonep_sizes& s, const int32_t* dst, const uint16_t
                      nvec, (int)s.recv_rows);
 }
 
-template <int KT, int U>
+template <int KT, int U, bool WEIGHTED>
 void launch_combine_ku(const moonep_sizes& s, const int32_t* dst, const float* w,
                        const uint16_t* y, uint16_t* out, int nvec, int threads, hipStream_t st) {
-  hipLaunchKernelGGL((combine_kernel<KT, U>), dim3((unsigned)s.T), dim3(threads), 0, st, dst,
+  hipLaunchKernelGGL((combine_kernel<KT, U, WEIGHTED>), dim3((unsigned)s.T), dim3(threads), 0, st, dst,
                      w, reinterpret_cast<const u32x4*>(y), reinterpret_cast<u32x4*>(out), s.K,
                      nvec, (int)s.recv_rows);
 }
 
-template <int KT>
+template <int KT, bool WEIGHTED>
 void launch_combine_k(const moonep_sizes& s, const int32_t* dst, const float* w,
                       const uint16_t* y, uint16_t* out, int nvec, int threads, int u,
                       hipStream_t st) {
   switch (u) {
-    case 1: launch_combine_ku<KT, 1>(s, dst, w, y, out, nvec, threads, st); break;
-    case 2: launch_combine_ku<KT, 2>(s, dst, w, y, out, nvec, threads, st); break;
-    case 3: launch_combine_ku<KT, 3>(s, dst, w, y, out, nvec, threads, st); break;
-    default: launch_combine_ku<KT, 4>(s, dst, w, y, out, nvec, threads, st); break;
+    case 1: launch_combine_ku<KT, 1, WEIGHTED>(s, dst, w, y, out, nvec, threads, st); break;
+    case 2: launch_combine_ku<KT, 2, WEIGHTED>(s, dst, w, y, out, nvec, threads, st); break;
+    case 3: launch_combine_ku<KT, 3, WEIGHTED>(s, dst, w, y, out, nvec, threads, st); break;
+    default: launch_combine_ku<KT, 4, WEIGHTED>(s, dst, w, y, out, nvec, threads, st); break;
   }
 }
 
@@ -247,20 +344,50 @@ hipError_t launch_dispatch(const moonep_sizes& s, const int32_t* plan, const uin
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const moonep_sizes& s, const int32_t* plan, const uint16_t* y,
-                          int H, uint16_t* out, hipStream_t st) {
+template <bool WEIGHTED>
+hipError_t launch_gather_sum(const moonep_sizes& s, const int32_t* plan, const uint16_t* y,
+                             int H, uint16_t* out, hipStream_t st) {
   const int nvec = H / 8;
   int threads = 64, u = 1;
   row_shape(nvec, 4, 2, &threads, &u);
   const int32_t* dst = plan + s.o_dst_row;
   const float* w = reinterpret_cast<const float*>(plan + s.o_w);
   switch (s.K) {
-    case 1: launch_combine_k<1>(s, dst, w, y, out, nvec, threads, u, st); break;
-    case 2: launch_combine_k<2>(s, dst, w, y, out, nvec, threads, u, st); break;
-    case 4: launch_combine_k<4>(s, dst, w, y, out, nvec, threads, u, st); break;
-    case 6: launch_combine_k<6>(s, dst, w, y, out, nvec, threads, u, st); break;
-    case 8: launch_combine_k<8>(s, dst, w, y, out, nvec, threads, u, st); break;
-    default: launch_combine_k<0>(s, dst, w, y, out, nvec, threads, u, st); break;
+    case 1: launch_combine_k<1, WEIGHTED>(s, dst, w, y, out, nvec, threads, u, st); break;
+    case 2: launch_combine_k<2, WEIGHTED>(s, dst, w, y, out, nvec, threads, u, st); break;
+    case 4: launch_combine_k<4, WEIGHTED>(s, dst, w, y, out, nvec, threads, u, st); break;
+    case 6: launch_combine_k<6, WEIGHTED>(s, dst, w, y, out, nvec, threads, u, st); break;
+    case 8: launch_combine_k<8, WEIGHTED>(s, dst, w, y, out, nvec, threads, u, st); break;
+    default: launch_combine_k<0, WEIGHTED>(s, dst, w, y, out, nvec, threads, u, st); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const moonep_sizes& s, const int32_t* plan, const uint16_t* y,
+                          int H, uint16_t* out, hipStream_t st) {
+  return launch_gather_sum<true>(s, plan, y, H, out, st);
+}
+
+hipError_t launch_dispatch_bwd(const moonep_sizes& s, const int32_t* plan, const uint16_t* g_recv,
+                               int H, uint16_t* gx, hipStream_t st) {
+  return launch_gather_sum<false>(s, plan, g_recv, H, gx, st);
+}
+
+hipError_t launch_combine_bwd(const moonep_sizes& s, const int32_t* plan, const uint16_t* dout,
+                              const uint16_t* y, int H, uint16_t* g_y, float* dw,
+                              hipStream_t st) {
+  const int nvec = H / 8;
+  int threads = 64, u = 1;
+  row_shape(nvec, 4, 2, &threads, &u);
+  const int32_t* dst = plan + s.o_dst_row;
+  const float* w = reinterpret_cast<const float*>(plan + s.o_w);
+  switch (s.K) {
+    case 1: launch_combine_bwd_k<1>(s, dst, w, dout, y, g_y, dw, nvec, threads, u, st); break;
+    case 2: launch_combine_bwd_k<2>(s, dst, w, dout, y, g_y, dw, nvec, threads, u, st); break;
+    case 4: launch_combine_bwd_k<4>(s, dst, w, dout, y, g_y, dw, nvec, threads, u, st); break;
+    case 6: launch_combine_bwd_k<6>(s, dst, w, dout, y, g_y, dw, nvec, threads, u, st); break;
+    case 8: launch_combine_bwd_k<8>(s, dst, w, dout, y, g_y, dw, nvec, threads, u, st); break;
+    default: launch_combine_bwd_k<MOONEP_MAX_K>(s, dst, w, dout, y, g_y, dw, nvec, threads, u, st); break;
   }
   return hipGetLastError();
 }

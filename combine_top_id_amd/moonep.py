@@ -60,18 +60,22 @@ def lib():
     L.moonep_dispatch.argtypes = [ctypes.POINTER(PlanDesc), vp, i32, vp, vp]
     L.moonep_combine.argtypes = [ctypes.POINTER(PlanDesc), vp, i32, vp, vp]
     L.moonep_reduce_grad.argtypes = [ctypes.POINTER(PlanDesc), vp, vp, i64, vp]
+    L.moonep_dispatch_bwd.argtypes = [ctypes.POINTER(PlanDesc), vp, i32, vp, vp]
+    L.moonep_combine_bwd.argtypes = [ctypes.POINTER(PlanDesc), vp, vp, i32, vp, vp, vp]
     L.moonep_plan_status.argtypes = [ctypes.POINTER(PlanDesc), ctypes.POINTER(PlanStats), vp]
     L.moonep_strerror.argtypes = [i32]
     L.moonep_strerror.restype = ctypes.c_char_p
     for f in ("moonep_query", "moonep_plan", "moonep_dispatch", "moonep_combine",
-              "moonep_reduce_grad", "moonep_plan_status"):
+              "moonep_reduce_grad", "moonep_plan_status", "moonep_dispatch_bwd",
+              "moonep_combine_bwd"):
         getattr(L, f).restype = i32
     _lib = L
     return L
 
 
 EXPORTS = ("moonep_query", "moonep_plan", "moonep_dispatch", "moonep_combine",
-           "moonep_reduce_grad", "moonep_plan_status", "moonep_strerror")
+           "moonep_reduce_grad", "moonep_plan_status", "moonep_strerror",
+           "moonep_dispatch_bwd", "moonep_combine_bwd")
 
 
 def _check(rc):
@@ -181,6 +185,39 @@ def moonep_combine(plan: Plan, y, out=None, stream=None):
     _check(lib().moonep_combine(ctypes.byref(plan.desc), _dev(y, torch.bfloat16, "y"), H,
                                 _dev(out, torch.bfloat16, "out"), _stream(stream)))
     return out
+
+
+def moonep_dispatch_bwd(plan: Plan, g_recv, gx=None, stream=None):
+    """gx[t] = bf16(sum_k g_recv[dst_row[t,k]]); g_recv bf16 [R*NvS, H] -> gx bf16 [T, H]."""
+    H = g_recv.shape[-1]
+    if g_recv.numel() != plan.sz.recv_rows * H:
+        raise MoonepError("g_recv must be [R*NvS, H]")
+    if gx is None:
+        gx = torch.empty(plan.sz.T, H, dtype=torch.bfloat16, device=g_recv.device)
+    if gx.numel() != plan.sz.T * H:
+        raise MoonepError("gx must be [T, H]")
+    _check(lib().moonep_dispatch_bwd(ctypes.byref(plan.desc), _dev(g_recv, torch.bfloat16, "g_recv"),
+                                     H, _dev(gx, torch.bfloat16, "gx"), _stream(stream)))
+    return gx
+
+
+def moonep_combine_bwd(plan: Plan, dout, y, g_y=None, dw=None, stream=None):
+    """g_y[dst_row[t,k]] = bf16(w[t,k] * dout[t]); dw[t,k] = <dout[t], y[dst_row[t,k]]>.
+    dout bf16 [T, H], y bf16 [R*NvS, H]; returns (g_y bf16 [R*NvS, H], dw fp32 [T, K])."""
+    H = dout.shape[-1]
+    if dout.numel() != plan.sz.T * H or y.numel() != plan.sz.recv_rows * H:
+        raise MoonepError("dout must be [T, H] and y [R*NvS, H]")
+    if g_y is None:
+        g_y = torch.empty(plan.sz.recv_rows, H, dtype=torch.bfloat16, device=dout.device)
+    if dw is None:
+        dw = torch.empty(plan.sz.T, plan.sz.K, dtype=torch.float32, device=dout.device)
+    if g_y.numel() != plan.sz.recv_rows * H or dw.numel() != plan.sz.T * plan.sz.K:
+        raise MoonepError("g_y must be [R*NvS, H] and dw [T, K]")
+    _check(lib().moonep_combine_bwd(ctypes.byref(plan.desc), _dev(dout, torch.bfloat16, "dout"),
+                                    _dev(y, torch.bfloat16, "y"), H,
+                                    _dev(g_y, torch.bfloat16, "g_y"),
+                                    _dev(dw, torch.float32, "dw"), _stream(stream)))
+    return g_y, dw
 
 
 def moonep_reduce_grad(plan: Plan, home_grad, rep_grad, stream=None):

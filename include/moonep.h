@@ -135,6 +135,29 @@ int moonep_dispatch(const moonep_plan_desc* plan, const uint16_t* x, int H, uint
 int moonep_combine(const moonep_plan_desc* plan, const uint16_t* y, int H, uint16_t* out,
                    hipStream_t stream);
 
+/* Backward of dispatch, reusing the forward plan ("MoonshotAI/MoonEP 딥다이브", section 4,
+ * design pattern 1: the plan serves both backward passes).  Dispatch copied x[t] into
+ * its K rows, so
+ *   gx[t, :] = bf16_rne( sum_{k=0..K-1} float(g_recv[dst_row[t,k], :]) )
+ * summed in fp32, k ascending.
+ *   g_recv  device bf16 [R*NvS, H] (gradient w.r.t. the dispatched rows)
+ *   gx      device bf16 [T, H]
+ * H % 8 == 0; both 16-byte aligned; gx must not overlap g_recv. */
+int moonep_dispatch_bwd(const moonep_plan_desc* plan, const uint16_t* g_recv, int H,
+                        uint16_t* gx, hipStream_t stream);
+
+/* Backward of combine, reusing the forward plan (same passage).  For
+ * out[t] = sum_k w[t,k] * y[dst_row[t,k]]:
+ *   g_y[dst_row[t,k], :] = bf16_rne( w[t,k] * float(dout[t, :]) )   (fp32 product)
+ *   dw[t, k]             = sum_h float(dout[t,h]) * float(y[dst_row[t,k], h])   (fp32, fused
+ *                          multiply-add, summation order unspecified)
+ *   dout  device bf16 [T, H];  y  device bf16 [R*NvS, H] (the forward expert outputs)
+ *   g_y   device bf16 [R*NvS, H], may be y itself (in place); padding rows untouched
+ *   dw    device fp32 [T, K]
+ * H % 8 == 0; dout, y, g_y 16-byte aligned. */
+int moonep_combine_bwd(const moonep_plan_desc* plan, const uint16_t* dout, const uint16_t* y,
+                       int H, uint16_t* g_y, float* dw, hipStream_t stream);
+
 /* Replica-gradient reduce (deep dive, section 4, design pattern 3: a replica's gradient
  * is kept apart and added to its home expert, so training equals no replication):
  *   for each expert e, for its slot pieces in creation order:
