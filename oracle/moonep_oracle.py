@@ -365,3 +365,45 @@ def combine_bwd(dst_row, w, dout_bits, y_bits, total_rows):
         yk = bf16_to_f32(y_bits[dst_row[:, k]]).astype(np.float64)
         dw[:, k] = (d32.astype(np.float64) * yk).sum(axis=1)
     return g_y, dw
+
+
+# ----------------------------------------------------------------------------------------
+# replica weight prefetch and the grouped expert stub (fallback pieces read home weights)
+# ----------------------------------------------------------------------------------------
+
+def prefetch_weight(p: Plan, home_w_bits):
+    """Copy each slot replica's home weights into the receiving rank's slot before expert
+    compute ([news, para 3]: duplicates are prefetched before computation starts;
+    [dive, section 3]: Buffer.prefetch_weight).  home_w [E, W_el] bf16 bits ->
+    slot_w [R, slots, W_el]; slots no piece uses stay zero here (unspecified)."""
+    sz = p.sz
+    home_w_bits = np.asarray(home_w_bits, dtype=np.uint16)
+    slot_w = np.zeros((sz.R, sz.slots, home_w_bits.shape[1]), dtype=np.uint16)
+    for (e, r, slot, cnt, start, fbpos) in p.pieces:
+        if slot >= 0:
+            slot_w[r, slot] = home_w_bits[e]
+    return slot_w
+
+
+def expert_stub(p: Plan, recv_bits, home_w_bits, slot_w_bits, H):
+    """A toy grouped expert over the rank buffers: y[row, h] = bf16(recv[row, h] * W[h])
+    for h < H, where W is the weight slab the row's group uses: its home expert's slab for
+    a home group, the rank's prefetched copy for a slot group, and the home slab read
+    across partitions for a fallback piece ([news, para 5]).  Rows no assignment maps to
+    stay zero here."""
+    sz = p.sz
+    y = np.zeros_like(recv_bits)
+
+    def apply(rows, w_bits):
+        w32 = bf16_to_f32(w_bits[:H])
+        y[rows] = f32_to_bf16_rne((bf16_to_f32(recv_bits[rows]) * w32).astype(np.float32))
+
+    for e in range(sz.E):
+        h = e // sz.E_loc
+        r0 = h * sz.NvS + int(p.off[h, e - h * sz.E_loc])
+        apply(np.arange(r0, r0 + int(p.keep[e])), home_w_bits[e])
+    for q in range(p.n_pieces):
+        e, r, slot, cnt = (int(v) for v in p.pieces[q, :4])
+        rows = np.arange(p.piece_row0(q), p.piece_row0(q) + cnt)
+        apply(rows, slot_w_bits[r, slot] if slot >= 0 else home_w_bits[e])
+    return y

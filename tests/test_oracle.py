@@ -553,3 +553,37 @@ def test_backward_round_trip_closed_form():
     assert (gx == O.f32_to_bf16_rne(acc)).all()
     # weights sum to one, so this is dout up to bf16 rounding of the K pieces
     assert_close(O.bf16_to_f32(gx), d32, 2 * 2.0 ** -8)
+
+
+# ----------------------------------------------------------------------------------------
+# prefetch and the grouped expert stub
+# ----------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("R,E,K,S,slots,skew,seed", [
+    (4, 16, 2, 64, 4, 0.2, 31),
+    (8, 64, 5, 100, 2, 0.05, 32),      # slots bind: fallback pieces read home weights
+])
+def test_prefetch_and_stub_equal_no_replication(R, E, K, S, slots, skew, seed):
+    rng = np.random.default_rng(seed)
+    ids = _random_loads(rng, R, E, K, S, skew)
+    p = O.plan(ids, R, E, K, S, slots)
+    assert p.n_replicas > 0
+    if seed == 32:
+        assert p.n_fallback > 0
+    H, W_el = 24, 40
+    dst = O.slot_map(p, ids)
+    x = O.f32_to_bf16_rne(rng.standard_normal((R * S, H)).astype(np.float32))
+    home_w = O.f32_to_bf16_rne(rng.standard_normal((E, W_el)).astype(np.float32))
+    slot_w = O.prefetch_weight(p, home_w)
+    # every used slot holds exactly its replica's home slab
+    for (e, r, slot, cnt, start, fbpos) in p.pieces:
+        if slot >= 0:
+            assert (slot_w[r, slot] == home_w[e]).all()
+    recv = O.dispatch(dst, x, R * p.sz.NvS)
+    y = O.expert_stub(p, recv, home_w, slot_w, H)
+    # no plan: assignment (t, k) applies its own expert to x[t]
+    for t in range(R * S):
+        for k in range(K):
+            e = ids[t, k]
+            ref = O.f32_to_bf16_rne((O.bf16_to_f32(x[t]) * O.bf16_to_f32(home_w[e, :H])).astype(np.float32))
+            assert (y[dst[t, k]] == ref).all()
