@@ -130,6 +130,7 @@ def main():
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-prefetch", action="store_true")
     ap.add_argument("--flush", choices=("auto", "on", "off"), default="auto",
                     help="write a 1 GiB buffer before every step so no input is served from "
                          "the 256 MB last-level cache (auto: when a step moves < 2 GB)")
@@ -285,6 +286,31 @@ def main():
                         bytes_per_token="combine_bwd (2K+1)*2H + 12K; dispatch_bwd (K+1)*2H + 4K")
         del g_y, dw, gx
 
+    # replica weight prefetch on the first batch's plan, DeepSeek-V3-shaped experts:
+    # three 7168 x 2048 bf16 matrices (88 MB) per expert
+    prefetch = None
+    if not args.no_prefetch:
+        W_el = 3 * 7168 * 2048
+        b0 = batches[0]
+        plan = M.moonep_plan(b0["ids"], b0["w"], wl.R, wl.E, wl.K, wl.S, wl.slots, plan=plan)
+        st0 = M.moonep_plan_status(plan)
+        home_w = torch.empty(wl.E, W_el, dtype=torch.bfloat16, device=dev)
+        slot_w = torch.empty(wl.R, wl.slots, W_el, dtype=torch.bfloat16, device=dev)
+        M.moonep_prefetch_weight(plan, home_w, slot_w)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        reps = 10
+        ev[0].record(stream)
+        for _ in range(reps):
+            M.moonep_prefetch_weight(plan, home_w, slot_w)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        tp = ev[0].elapsed_time(ev[1]) * 1e3 / reps
+        pb = st0["n_replicas"] * 2 * W_el * 2
+        prefetch = dict(replicas=st0["n_replicas"], expert_bytes=2 * W_el, prefetch_us=round(tp, 2),
+                        gbps=round(pb / tp / 1e3, 1) if st0["n_replicas"] else None)
+        del home_w, slot_w
+
     # a plain device copy of 4 GiB as a measured ceiling on the same box
     a = torch.empty(1 << 31, dtype=torch.int16, device=dev)
     c = torch.empty_like(a)
@@ -339,6 +365,7 @@ def main():
         "plan_us_median": round(statistics.median([r["plan_us"] for r in rows]), 2),
         "copy_ceiling_gbps": round(copy_gbps, 1),
         "backward": backward,
+        "prefetch": prefetch,
     }
     if not args.no_cpu_baseline:
         b0 = batches[0]

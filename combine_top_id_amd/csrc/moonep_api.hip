@@ -109,6 +109,35 @@ int moonep_reduce_grad(const moonep_plan_desc* plan, float* home_grad, const flo
   return err == hipSuccess ? MOONEP_OK : MOONEP_EHIP;
 }
 
+int moonep_prefetch_weight(const moonep_plan_desc* plan, const uint16_t* home_w, int64_t W_el,
+                           uint16_t* slot_w, hipStream_t stream) {
+  const int rc = check_desc(plan);
+  if (rc != MOONEP_OK) return rc;
+  if (!home_w || W_el <= 0 || W_el % 8 != 0) return MOONEP_EINVAL;
+  if (plan->sz.slots > 0 && !slot_w) return MOONEP_EINVAL;
+  if (!aligned(home_w, 16) || (slot_w && !aligned(slot_w, 16))) return MOONEP_EALIGN;
+  if (plan->sz.slots == 0) return MOONEP_OK;
+  const hipError_t err = launch_prefetch(plan->sz, static_cast<const int32_t*>(plan->dev), home_w,
+                                         W_el, slot_w, stream);
+  return err == hipSuccess ? MOONEP_OK : MOONEP_EHIP;
+}
+
+int moonep_expert_stub(const moonep_plan_desc* plan, const int32_t* topk_ids,
+                       const uint16_t* recv, const uint16_t* home_w, const uint16_t* slot_w,
+                       int64_t W_el, int H, uint16_t* y, hipStream_t stream) {
+  const int rc = check_desc(plan);
+  if (rc != MOONEP_OK) return rc;
+  if (!topk_ids || !recv || !home_w || !y || H <= 0 || H % 8 != 0 || W_el < H || W_el % 8 != 0)
+    return MOONEP_EINVAL;
+  if (plan->sz.slots > 0 && !slot_w) return MOONEP_EINVAL;
+  if (!aligned(recv, 16) || !aligned(home_w, 16) || !aligned(y, 16) || !aligned(topk_ids, 4) ||
+      (slot_w && !aligned(slot_w, 16)))
+    return MOONEP_EALIGN;
+  const hipError_t err = launch_expert_stub(plan->sz, static_cast<const int32_t*>(plan->dev),
+                                            topk_ids, recv, home_w, slot_w, W_el, H, y, stream);
+  return err == hipSuccess ? MOONEP_OK : MOONEP_EHIP;
+}
+
 int moonep_plan_status(const moonep_plan_desc* plan, moonep_plan_stats* out,
                        hipStream_t stream) {
   const int rc = check_desc(plan);

@@ -97,6 +97,12 @@ hipError_t launch_dispatch_bwd(const moonep_sizes& s, const int32_t* plan, const
 hipError_t launch_combine_bwd(const moonep_sizes& s, const int32_t* plan, const uint16_t* dout,
                               const uint16_t* y, int H, uint16_t* g_y, float* dw,
                               hipStream_t st);
+hipError_t launch_prefetch(const moonep_sizes& s, const int32_t* plan, const uint16_t* home_w,
+                           int64_t W_el, uint16_t* slot_w, hipStream_t st);
+hipError_t launch_expert_stub(const moonep_sizes& s, const int32_t* plan, const int32_t* ids,
+                              const uint16_t* recv, const uint16_t* home_w,
+                              const uint16_t* slot_w, int64_t W_el, int H, uint16_t* y,
+                              hipStream_t st);
 hipError_t launch_reduce(const moonep_sizes& s, const int32_t* plan, float* home,
                          const float* rep, int64_t G_el, hipStream_t st);
 

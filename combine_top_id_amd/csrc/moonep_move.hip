@@ -227,6 +227,98 @@ void launch_combine_bwd_k(const moonep_sizes& s, const int32_t* dst, const float
 }
 
 // ---------------------------------------------------------------------------------------
+// replica weight prefetch: slot_w[r_p][slot_p] = home_w[e_p] for every slot piece p
+// ---------------------------------------------------------------------------------------
+// Persistent grid over (piece, 16 KB chunk) items; the piece count comes from the plan
+// header, so the host never waits for the plan.  Fallback pieces own no slot: skipped.
+constexpr int kCopyThreads = 256;
+constexpr int kCopyU = 4;
+constexpr int kCopyChunk = kCopyThreads * kCopyU;     // 16-byte vectors per item
+
+__global__ __launch_bounds__(kCopyThreads) void prefetch_kernel(const int32_t* __restrict__ plan,
+                                                                const u32x4* __restrict__ home,
+                                                                u32x4* __restrict__ slotw,
+                                                                int64_t wv, const moonep_sizes s) {
+  const int np = plan[s.o_hdr + H_STATUS] == 0 ? plan[s.o_hdr + H_NPIECES] : 0;
+  const int64_t nchunk = (wv + kCopyChunk - 1) / kCopyChunk;
+  const int64_t items = (int64_t)np * nchunk;
+  const int32_t* pieces = plan + s.o_pieces;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int p = (int)(it / nchunk);
+    const int64_t c = it - (int64_t)p * nchunk;
+    const int32_t* pc = pieces + (int64_t)p * kPieceInts;
+    const int slot = pc[P_SLOT], r = pc[P_R], e = pc[P_E];
+    if (slot < 0 || slot >= s.slots || (unsigned)r >= (unsigned)s.R || (unsigned)e >= (unsigned)s.E)
+      continue;
+    const u32x4* src = home + (int64_t)e * wv;
+    u32x4* dstp = slotw + ((int64_t)r * s.slots + slot) * wv;
+    u32x4 v[kCopyU];
+#pragma unroll
+    for (int u = 0; u < kCopyU; ++u) {
+      const int64_t i = c * kCopyChunk + u * kCopyThreads + threadIdx.x;
+      if (i < wv) v[u] = __builtin_nontemporal_load(src + i);
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyU; ++u) {
+      const int64_t i = c * kCopyChunk + u * kCopyThreads + threadIdx.x;
+      if (i < wv) __builtin_nontemporal_store(v[u], dstp + i);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// expert stub: y[row, h] = bf16(recv[row, h] * W[h]) for h < H, with W the weight slab the
+// row's group uses (home group: home_w[e]; slot group: the rank's prefetched slot_w copy;
+// fallback piece: home_w[e], read across partitions)
+// ---------------------------------------------------------------------------------------
+// One workgroup per token; each assignment's row and expert come from dst_row and the
+// caller's topk_ids, its weight source from the packed expert and piece tables.
+__global__ __launch_bounds__(256) void expert_stub_kernel(const int32_t* __restrict__ plan,
+                                                          const int32_t* __restrict__ ids,
+                                                          const u32x4* __restrict__ recv,
+                                                          const u32x4* __restrict__ home,
+                                                          const u32x4* __restrict__ slotw,
+                                                          int64_t wv, u32x4* __restrict__ y,
+                                                          int nvec, const moonep_sizes s) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const int64_t t = blockIdx.x;
+  const int32_t* dst = plan + s.o_dst_row;
+  const i32x4* xtab = reinterpret_cast<const i32x4*>(plan + s.o_xtab);
+  const int32_t* pieces = plan + s.o_pieces;
+  const int nrows = (int)s.recv_rows;
+  for (int k = 0; k < s.K; ++k) {
+    const int row = dst[t * s.K + k];
+    const int e = ids[t * s.K + k];
+    if ((unsigned)row >= (unsigned)nrows || (unsigned)e >= (unsigned)s.E) continue;
+    const i32x4 xt = xtab[e];                    // keep, home row, first piece, count
+    const u32x4* w = home + (int64_t)e * wv;     // home group, or fallback (remote read)
+    if (row < xt.y || row >= xt.y + xt.x) {
+      for (int q = xt.z; q < xt.z + xt.w; ++q) {
+        const int32_t* pc = pieces + (int64_t)q * kPieceInts;
+        if (row >= pc[P_ROW0] && row < pc[P_ROW0] + pc[P_CNT]) {
+          if (pc[P_SLOT] >= 0 && pc[P_SLOT] < s.slots)
+            w = slotw + ((int64_t)pc[P_R] * s.slots + pc[P_SLOT]) * wv;
+          break;
+        }
+      }
+    }
+    const u32x4* src = recv + (int64_t)row * nvec;
+    u32x4* out = y + (int64_t)row * nvec;
+    for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
+      const u32x4 a = src[v], b = w[v];
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float lo = bf_lo(a[q]) * bf_lo(b[q]);
+        const float hi = bf_hi(a[q]) * bf_hi(b[q]);
+        o[q] = to_bf16(lo) | (to_bf16(hi) << 16);
+      }
+      out[v] = o;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // reduce: home[e] += rep[r_p][slot_p] for each slot piece p of e, in creation order
 // ---------------------------------------------------------------------------------------
 // A persistent grid walks (expert with replicas, chunk) items; the item count lives on
@@ -389,6 +481,25 @@ hipError_t launch_combine_bwd(const moonep_sizes& s, const int32_t* plan, const 
     case 8: launch_combine_bwd_k<8>(s, dst, w, dout, y, g_y, dw, nvec, threads, u, st); break;
     default: launch_combine_bwd_k<MOONEP_MAX_K>(s, dst, w, dout, y, g_y, dw, nvec, threads, u, st); break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefetch(const moonep_sizes& s, const int32_t* plan, const uint16_t* home_w,
+                           int64_t W_el, uint16_t* slot_w, hipStream_t st) {
+  hipLaunchKernelGGL(prefetch_kernel, dim3(2048), dim3(kCopyThreads), 0, st, plan,
+                     reinterpret_cast<const u32x4*>(home_w), reinterpret_cast<u32x4*>(slot_w),
+                     W_el / 8, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_stub(const moonep_sizes& s, const int32_t* plan, const int32_t* ids,
+                              const uint16_t* recv, const uint16_t* home_w,
+                              const uint16_t* slot_w, int64_t W_el, int H, uint16_t* y,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(expert_stub_kernel, dim3((unsigned)s.T), dim3(256), 0, st, plan, ids,
+                     reinterpret_cast<const u32x4*>(recv), reinterpret_cast<const u32x4*>(home_w),
+                     reinterpret_cast<const u32x4*>(slot_w), W_el / 8,
+                     reinterpret_cast<u32x4*>(y), H / 8, s);
   return hipGetLastError();
 }
 

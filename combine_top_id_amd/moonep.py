@@ -62,12 +62,14 @@ def lib():
     L.moonep_reduce_grad.argtypes = [ctypes.POINTER(PlanDesc), vp, vp, i64, vp]
     L.moonep_dispatch_bwd.argtypes = [ctypes.POINTER(PlanDesc), vp, i32, vp, vp]
     L.moonep_combine_bwd.argtypes = [ctypes.POINTER(PlanDesc), vp, vp, i32, vp, vp, vp]
+    L.moonep_prefetch_weight.argtypes = [ctypes.POINTER(PlanDesc), vp, i64, vp, vp]
+    L.moonep_expert_stub.argtypes = [ctypes.POINTER(PlanDesc), vp, vp, vp, vp, i64, i32, vp, vp]
     L.moonep_plan_status.argtypes = [ctypes.POINTER(PlanDesc), ctypes.POINTER(PlanStats), vp]
     L.moonep_strerror.argtypes = [i32]
     L.moonep_strerror.restype = ctypes.c_char_p
     for f in ("moonep_query", "moonep_plan", "moonep_dispatch", "moonep_combine",
               "moonep_reduce_grad", "moonep_plan_status", "moonep_dispatch_bwd",
-              "moonep_combine_bwd"):
+              "moonep_combine_bwd", "moonep_prefetch_weight", "moonep_expert_stub"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -75,7 +77,8 @@ def lib():
 
 EXPORTS = ("moonep_query", "moonep_plan", "moonep_dispatch", "moonep_combine",
            "moonep_reduce_grad", "moonep_plan_status", "moonep_strerror",
-           "moonep_dispatch_bwd", "moonep_combine_bwd")
+           "moonep_dispatch_bwd", "moonep_combine_bwd", "moonep_prefetch_weight",
+           "moonep_expert_stub")
 
 
 def _check(rc):
@@ -218,6 +221,38 @@ def moonep_combine_bwd(plan: Plan, dout, y, g_y=None, dw=None, stream=None):
                                     _dev(g_y, torch.bfloat16, "g_y"),
                                     _dev(dw, torch.float32, "dw"), _stream(stream)))
     return g_y, dw
+
+
+def moonep_prefetch_weight(plan: Plan, home_w, slot_w=None, stream=None):
+    """slot_w[r, slot] = home_w[e] for every slot piece; home_w bf16 [E, W_el] ->
+    slot_w bf16 [R, slots, W_el]."""
+    W_el = home_w.shape[-1]
+    if home_w.numel() != plan.sz.E * W_el:
+        raise MoonepError("home_w must be [E, W_el]")
+    if slot_w is None:
+        slot_w = torch.empty(plan.sz.R, plan.sz.slots, W_el, dtype=torch.bfloat16,
+                             device=home_w.device)
+    if slot_w.numel() != plan.sz.R * plan.sz.slots * W_el:
+        raise MoonepError("slot_w must be [R, slots, W_el]")
+    sp = _dev(slot_w, torch.bfloat16, "slot_w") if slot_w.numel() else ctypes.c_void_p(0)
+    _check(lib().moonep_prefetch_weight(ctypes.byref(plan.desc),
+                                        _dev(home_w, torch.bfloat16, "home_w"), W_el, sp,
+                                        _stream(stream)))
+    return slot_w
+
+
+def moonep_expert_stub(plan: Plan, topk_ids, recv, home_w, slot_w, y=None, stream=None):
+    """y[row] = bf16(recv[row] * W[:H]) with W the weight slab the row's group reads."""
+    H = recv.shape[-1]
+    W_el = home_w.shape[-1]
+    if y is None:
+        y = torch.empty_like(recv)
+    sp = _dev(slot_w, torch.bfloat16, "slot_w") if slot_w.numel() else ctypes.c_void_p(0)
+    _check(lib().moonep_expert_stub(ctypes.byref(plan.desc), _dev(topk_ids, torch.int32, "topk_ids"),
+                                    _dev(recv, torch.bfloat16, "recv"),
+                                    _dev(home_w, torch.bfloat16, "home_w"), sp, W_el, H,
+                                    _dev(y, torch.bfloat16, "y"), _stream(stream)))
+    return y
 
 
 def moonep_reduce_grad(plan: Plan, home_grad, rep_grad, stream=None):

@@ -168,6 +168,31 @@ int moonep_combine_bwd(const moonep_plan_desc* plan, const uint16_t* dout, const
 int moonep_reduce_grad(const moonep_plan_desc* plan, float* home_grad, const float* rep_grad,
                        int64_t G_el, hipStream_t stream);
 
+/* Replica weight prefetch ("Moonshot AI Open-Sources MoonEP", paragraph 3: the duplicated
+ * experts are prefetched before computation starts; "MoonshotAI/MoonEP 딥다이브", section 3:
+ * Buffer.prefetch_weight):
+ *   for every slot piece p of the plan:  slot_w[r_p, slot_p, :] = home_w[e_p, :]  (bit copy)
+ *   home_w  device bf16 [E, W_el] (each expert's weights, any layout, W_el elements)
+ *   slot_w  device bf16 [R, slots, W_el]; slots no piece uses are not written
+ * W_el % 8 == 0; both 16-byte aligned; slot_w must not overlap home_w.  Fallback pieces
+ * own no slot: their rank reads home_w directly (see moonep_expert_stub). */
+int moonep_prefetch_weight(const moonep_plan_desc* plan, const uint16_t* home_w, int64_t W_el,
+                           uint16_t* slot_w, hipStream_t stream);
+
+/* A toy expert that checks which weights each buffer group reads ("Moonshot AI
+ * Open-Sources MoonEP", paragraph 5: without a free slot the rank falls back to remote
+ * reads of the home expert):
+ *   y[row, h] = bf16_rne( float(recv[row, h]) * float(W[h]) ),  h < H,
+ * for every mapped row, where W is home_w[e] for a home group, slot_w[r, slot] for a slot
+ * group and home_w[e] (read across partitions) for a fallback piece.  The row's expert e
+ * comes from the caller's topk_ids (the same array given to moonep_plan).
+ *   topk_ids int32 [T, K];  recv, y  bf16 [R*NvS, H];  home_w bf16 [E, W_el];
+ *   slot_w bf16 [R, slots, W_el]  (W_el >= H, W_el % 8 == 0, H % 8 == 0)
+ * Padding rows of y are not written. */
+int moonep_expert_stub(const moonep_plan_desc* plan, const int32_t* topk_ids,
+                       const uint16_t* recv, const uint16_t* home_w, const uint16_t* slot_w,
+                       int64_t W_el, int H, uint16_t* y, hipStream_t stream);
+
 /* Waits for `stream`, then copies the plan's statistics to the host.  The only call
  * that synchronises. */
 int moonep_plan_status(const moonep_plan_desc* plan, moonep_plan_stats* out,
