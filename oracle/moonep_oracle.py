@@ -407,3 +407,30 @@ def expert_stub(p: Plan, recv_bits, home_w_bits, slot_w_bits, H):
         rows = np.arange(p.piece_row0(q), p.piece_row0(q) + cnt)
         apply(rows, slot_w_bits[r, slot] if slot >= 0 else home_w_bits[e])
     return y
+
+
+# ----------------------------------------------------------------------------------------
+# staged (non-zero-copy) dispatch and combine: the copies zero-copy removes
+# ----------------------------------------------------------------------------------------
+
+def dispatch_staged(dst_row, x_bits, total_rows):
+    """Rows first land in a staging buffer in arrival order, stage[t*K + k] = x[t]; an
+    epilogue then permutes them into their final rows, recv[dst_row[t, k]] =
+    stage[t*K + k] ([dive, section 2, point 2]: the receive-then-permute-and-copy scheme
+    zero-copy replaces; section 8, exercise D).  Returns (stage, recv)."""
+    dst_row = np.asarray(dst_row)
+    T, K = dst_row.shape
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    stage = x_bits[np.repeat(np.arange(T), K)]
+    recv = np.zeros((total_rows, x_bits.shape[1]), dtype=np.uint16)
+    recv[dst_row.reshape(-1)] = stage
+    return stage, recv
+
+
+def combine_staged(dst_row, w, y_bits):
+    """Prologue: stage[t*K + k] = y[dst_row[t, k]] (expert outputs gathered back into
+    arrival order), then the weighted combine reads the staging buffer in order."""
+    dst_row = np.asarray(dst_row)
+    T, K = dst_row.shape
+    stage = np.asarray(y_bits, dtype=np.uint16)[dst_row.reshape(-1)]
+    return stage, combine(np.arange(T * K).reshape(T, K), w, stage)

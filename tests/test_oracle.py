@@ -587,3 +587,18 @@ def test_prefetch_and_stub_equal_no_replication(R, E, K, S, slots, skew, seed):
             e = ids[t, k]
             ref = O.f32_to_bf16_rne((O.bf16_to_f32(x[t]) * O.bf16_to_f32(home_w[e, :H])).astype(np.float32))
             assert (y[dst[t, k]] == ref).all()
+
+
+def test_staged_equals_zero_copy():
+    w, ids, wt, x = _tiny_inputs(seed=20260105)
+    p = O.plan(ids, w.R, w.E, w.K, w.S, w.slots)
+    dst = O.slot_map(p, ids)
+    rows = w.R * p.sz.NvS
+    stage, recv_s = O.dispatch_staged(dst, x, rows)
+    recv = O.dispatch(dst, x, rows)
+    assert (recv_s == recv).all()
+    # arrival order: assignment i's staging row holds token i // K
+    assert (stage == x[np.arange(w.T * w.K) // w.K]).all()
+    stage_c, out_s = O.combine_staged(dst, wt, recv)
+    assert (out_s == O.combine(dst, wt, recv)).all()
+    assert (stage_c == recv[dst.reshape(-1)]).all()
