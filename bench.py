@@ -131,6 +131,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-prefetch", action="store_true")
+    ap.add_argument("--no-staged", action="store_true")
     ap.add_argument("--flush", choices=("auto", "on", "off"), default="auto",
                     help="write a 1 GiB buffer before every step so no input is served from "
                          "the 256 MB last-level cache (auto: when a step moves < 2 GB)")
@@ -286,6 +287,38 @@ def main():
                         bytes_per_token="combine_bwd (2K+1)*2H + 12K; dispatch_bwd (K+1)*2H + 4K")
         del g_y, dw, gx
 
+    # zero-copy vs staged (non-zero-copy) A/B on the first batch: the staged path adds an
+    # epilogue row copy to dispatch and a prologue row copy to combine
+    staged = None
+    if not args.no_staged:
+        b0 = batches[0]
+        plan = M.moonep_plan(b0["ids"], b0["w"], wl.R, wl.E, wl.K, wl.S, wl.slots, plan=plan)
+        stage = torch.empty(wl.A, wl.H, dtype=torch.bfloat16, device=dev)
+        M.moonep_dispatch_staged(plan, b0["x"], recv, stage)
+        M.moonep_combine_staged(plan, recv, out, stage)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        reps = 10
+        ev[0].record(stream)
+        for _ in range(reps):
+            M.moonep_dispatch(plan, b0["x"], recv)
+        ev[1].record(stream)
+        for _ in range(reps):
+            M.moonep_dispatch_staged(plan, b0["x"], recv, stage)
+        ev[2].record(stream)
+        for _ in range(reps):
+            M.moonep_combine(plan, recv, out)
+        ev[3].record(stream)
+        for _ in range(reps):
+            M.moonep_combine_staged(plan, recv, out, stage)
+        ev[4].record(stream)
+        torch.cuda.synchronize()
+        t = [ev[i].elapsed_time(ev[i + 1]) * 1e3 / reps for i in range(4)]
+        staged = dict(dispatch_zero_copy_us=round(t[0], 2), dispatch_staged_us=round(t[1], 2),
+                      combine_zero_copy_us=round(t[2], 2), combine_staged_us=round(t[3], 2),
+                      staged_over_zero_copy=round((t[1] + t[3]) / (t[0] + t[2]), 3))
+        del stage
+
     # replica weight prefetch on the first batch's plan, DeepSeek-V3-shaped experts:
     # three 7168 x 2048 bf16 matrices (88 MB) per expert
     prefetch = None
@@ -366,6 +399,7 @@ def main():
         "copy_ceiling_gbps": round(copy_gbps, 1),
         "backward": backward,
         "prefetch": prefetch,
+        "zero_copy_ab": staged,
     }
     if not args.no_cpu_baseline:
         b0 = batches[0]

@@ -4,5 +4,6 @@ weighted combine -> replica-gradient reduce, as HIP kernels behind a C ABI
 
 from .moonep import (moonep_query, moonep_plan, moonep_dispatch, moonep_combine,  # noqa: F401
                      moonep_reduce_grad, moonep_plan_status, moonep_dispatch_bwd,
-                     moonep_combine_bwd, moonep_prefetch_weight, moonep_expert_stub, Plan,
+                     moonep_combine_bwd, moonep_prefetch_weight, moonep_expert_stub,
+                     moonep_dispatch_staged, moonep_combine_staged, Plan,
                      Sizes, MoonepError, lib, LIB_PATH, EXPORTS)

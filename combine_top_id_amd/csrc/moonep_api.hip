@@ -73,6 +73,28 @@ int moonep_combine(const moonep_plan_desc* plan, const uint16_t* y, int H, uint1
   return err == hipSuccess ? MOONEP_OK : MOONEP_EHIP;
 }
 
+int moonep_dispatch_staged(const moonep_plan_desc* plan, const uint16_t* x, int H,
+                           uint16_t* stage, uint16_t* recv, hipStream_t stream) {
+  const int rc = check_desc(plan);
+  if (rc != MOONEP_OK) return rc;
+  if (!x || !stage || !recv || H <= 0 || H % 8 != 0) return MOONEP_EINVAL;
+  if (!aligned(x, 16) || !aligned(stage, 16) || !aligned(recv, 16)) return MOONEP_EALIGN;
+  const hipError_t err = launch_dispatch_staged(plan->sz, static_cast<const int32_t*>(plan->dev),
+                                                x, H, stage, recv, stream);
+  return err == hipSuccess ? MOONEP_OK : MOONEP_EHIP;
+}
+
+int moonep_combine_staged(const moonep_plan_desc* plan, const uint16_t* y, int H,
+                          uint16_t* stage, uint16_t* out, hipStream_t stream) {
+  const int rc = check_desc(plan);
+  if (rc != MOONEP_OK) return rc;
+  if (!y || !stage || !out || H <= 0 || H % 8 != 0) return MOONEP_EINVAL;
+  if (!aligned(y, 16) || !aligned(stage, 16) || !aligned(out, 16)) return MOONEP_EALIGN;
+  const hipError_t err = launch_combine_staged(plan->sz, static_cast<const int32_t*>(plan->dev),
+                                               y, H, stage, out, stream);
+  return err == hipSuccess ? MOONEP_OK : MOONEP_EHIP;
+}
+
 int moonep_dispatch_bwd(const moonep_plan_desc* plan, const uint16_t* g_recv, int H,
                         uint16_t* gx, hipStream_t stream) {
   const int rc = check_desc(plan);

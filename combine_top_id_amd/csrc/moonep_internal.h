@@ -92,6 +92,10 @@ hipError_t launch_dispatch(const moonep_sizes& s, const int32_t* plan, const uin
                            int H, uint16_t* recv, hipStream_t st);
 hipError_t launch_combine(const moonep_sizes& s, const int32_t* plan, const uint16_t* y,
                           int H, uint16_t* out, hipStream_t st);
+hipError_t launch_dispatch_staged(const moonep_sizes& s, const int32_t* plan, const uint16_t* x,
+                                  int H, uint16_t* stage, uint16_t* recv, hipStream_t st);
+hipError_t launch_combine_staged(const moonep_sizes& s, const int32_t* plan, const uint16_t* y,
+                                 int H, uint16_t* stage, uint16_t* out, hipStream_t st);
 hipError_t launch_dispatch_bwd(const moonep_sizes& s, const int32_t* plan, const uint16_t* g_recv,
                                int H, uint16_t* gx, hipStream_t st);
 hipError_t launch_combine_bwd(const moonep_sizes& s, const int32_t* plan, const uint16_t* dout,

@@ -25,6 +25,23 @@ __device__ __forceinline__ unsigned int to_bf16(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Threads per workgroup (a multiple of 64, at most 1024) and vectors per thread (at most
+// umax) for a row of nvec 16-byte vectors: the fewest idle lanes first, then the vectors
+// per thread closest to upref, then the most threads.
+void row_shape(int nvec, int umax, int upref, int* threads, int* u) {
+  long best[3] = {-1, 0, 0};
+  for (int t = 64; t <= 1024; t += 64) {
+    for (int uu = 1; uu <= umax; ++uu) {
+      const long cover = (long)t * uu;
+      const long waste = (nvec + cover - 1) / cover * cover - nvec;
+      const long d = uu > upref ? uu - upref : upref - uu;
+      const bool better = best[0] < 0 || waste < best[0] ||
+                          (waste == best[0] && (d < best[1] || (d == best[1] && t > *threads)));
+      if (better) { best[0] = waste; best[1] = d; *threads = t; *u = uu; }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------------
 // dispatch: recv[dst_row[t, k]] = x[t]
 // ---------------------------------------------------------------------------------------
@@ -37,7 +54,7 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t* __restric
                                                        u32x4* __restrict__ recv, int K,
                                                        int nvec, int nrows) {
   const int64_t t = blockIdx.x;
-  const int32_t* d = dst + t * K;
+  const int32_t* d = dst ? dst + t * K : nullptr;   // null: staging row t*K + k
   const u32x4* src = x + t * nvec;
   const int step = blockDim.x * U;
   for (int v0 = threadIdx.x; v0 < nvec; v0 += step) {
@@ -48,7 +65,7 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t* __restric
       if (v < nvec) buf[u] = src[v];
     }
     for (int k = 0; k < K; ++k) {
-      const int row = d[k];
+      const int row = d ? d[k] : (int)(t * K + k);
       if ((unsigned)row >= (unsigned)nrows) continue;   // -1: unmapped
       u32x4* o = recv + (int64_t)row * nvec;
 #pragma unroll
@@ -99,7 +116,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(const int32_t* __restrict
                                                       int nvec, int nrows) {
   const int K = KT > 0 ? KT : Krt;
   const int64_t t = blockIdx.x;
-  const int32_t* d = dst + t * K;
+  const int32_t* d = dst ? dst + t * K : nullptr;   // null: staging row t*K + k
   const float* wt = wts + t * K;
   const int step = blockDim.x * U;
   for (int v0 = threadIdx.x; v0 < nvec; v0 += step) {
@@ -111,10 +128,12 @@ __global__ __launch_bounds__(1024) void combine_kernel(const int32_t* __restrict
     if constexpr (KT > 0) {
 #pragma unroll
       for (int k = 0; k < KT; ++k)
-        combine_accumulate<U, WEIGHTED>(acc, y, d[k], WEIGHTED ? wt[k] : 1.f, v0, nvec, nrows);
+        combine_accumulate<U, WEIGHTED>(acc, y, d ? d[k] : (int)(t * K + k),
+                                        WEIGHTED ? wt[k] : 1.f, v0, nvec, nrows);
     } else {
       for (int k = 0; k < K; ++k)
-        combine_accumulate<U, WEIGHTED>(acc, y, d[k], WEIGHTED ? wt[k] : 1.f, v0, nvec, nrows);
+        combine_accumulate<U, WEIGHTED>(acc, y, d ? d[k] : (int)(t * K + k),
+                                        WEIGHTED ? wt[k] : 1.f, v0, nvec, nrows);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -223,6 +242,62 @@ void launch_combine_bwd_k(const moonep_sizes& s, const int32_t* dst, const float
     case 2: hipLaunchKernelGGL((combine_bwd_kernel<KMAX, 2>), grid, block, 0, st, dst, w, dv, yv, gv, dw, s.K, nvec, nrows); break;
     case 3: hipLaunchKernelGGL((combine_bwd_kernel<KMAX, 3>), grid, block, 0, st, dst, w, dv, yv, gv, dw, s.K, nvec, nrows); break;
     default: hipLaunchKernelGGL((combine_bwd_kernel<KMAX, 4>), grid, block, 0, st, dst, w, dv, yv, gv, dw, s.K, nvec, nrows); break;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// staged (non-zero-copy) mode: the row copies zero-copy removes
+// ---------------------------------------------------------------------------------------
+// EPILOGUE: recv[dst_row[t,k]] = stage[t*K + k]  (staging buffer -> final rows)
+// PROLOGUE: stage[t*K + k] = y[dst_row[t,k]]     (final rows -> staging buffer)
+template <int U, bool EPILOGUE>
+__global__ __launch_bounds__(1024) void copy_rows_kernel(const int32_t* __restrict__ dst,
+                                                         const u32x4* __restrict__ src,
+                                                         u32x4* __restrict__ out, int K,
+                                                         int nvec, int nrows) {
+  const int64_t t = blockIdx.x;
+  const int32_t* d = dst + t * K;
+  for (int k = 0; k < K; ++k) {
+    const int r = d[k];
+    if ((unsigned)r >= (unsigned)nrows) continue;      // -1: unmapped
+    const int64_t srow = EPILOGUE ? t * K + k : r;
+    const int64_t drow = EPILOGUE ? r : t * K + k;
+    const u32x4* sp = src + srow * nvec;
+    u32x4* op = out + drow * nvec;
+    for (int v0 = threadIdx.x; v0 < nvec; v0 += blockDim.x * U) {
+      u32x4 buf[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + u * blockDim.x;
+        if (v < nvec) buf[u] = sp[v];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + u * blockDim.x;
+        if (v < nvec) op[v] = buf[u];
+      }
+    }
+  }
+}
+
+template <bool EPILOGUE>
+void launch_copy_rows(const moonep_sizes& s, const int32_t* dst, const uint16_t* src, uint16_t* out,
+                      int nvec, hipStream_t st) {
+  int threads = 64, u = 1;
+  row_shape(nvec, 8, 7, &threads, &u);
+  const dim3 grid((unsigned)s.T), block(threads);
+  const u32x4* sv = reinterpret_cast<const u32x4*>(src);
+  u32x4* ov = reinterpret_cast<u32x4*>(out);
+  const int nrows = (int)s.recv_rows;
+  switch (u) {
+    case 1: hipLaunchKernelGGL((copy_rows_kernel<1, EPILOGUE>), grid, block, 0, st, dst, sv, ov, s.K, nvec, nrows); break;
+    case 2: hipLaunchKernelGGL((copy_rows_kernel<2, EPILOGUE>), grid, block, 0, st, dst, sv, ov, s.K, nvec, nrows); break;
+    case 3: hipLaunchKernelGGL((copy_rows_kernel<3, EPILOGUE>), grid, block, 0, st, dst, sv, ov, s.K, nvec, nrows); break;
+    case 4: hipLaunchKernelGGL((copy_rows_kernel<4, EPILOGUE>), grid, block, 0, st, dst, sv, ov, s.K, nvec, nrows); break;
+    case 5: hipLaunchKernelGGL((copy_rows_kernel<5, EPILOGUE>), grid, block, 0, st, dst, sv, ov, s.K, nvec, nrows); break;
+    case 6: hipLaunchKernelGGL((copy_rows_kernel<6, EPILOGUE>), grid, block, 0, st, dst, sv, ov, s.K, nvec, nrows); break;
+    case 7: hipLaunchKernelGGL((copy_rows_kernel<7, EPILOGUE>), grid, block, 0, st, dst, sv, ov, s.K, nvec, nrows); break;
+    default: hipLaunchKernelGGL((copy_rows_kernel<8, EPILOGUE>), grid, block, 0, st, dst, sv, ov, s.K, nvec, nrows); break;
   }
 }
 
@@ -370,29 +445,13 @@ __global__ __launch_bounds__(kRedThreads) void reduce_kernel(const int32_t* __re
   }
 }
 
-// Threads per workgroup (a multiple of 64, at most 1024) and vectors per thread (at most
-// umax) for a row of nvec 16-byte vectors: the fewest idle lanes first, then the vectors
-// per thread closest to upref, then the most threads.
-void row_shape(int nvec, int umax, int upref, int* threads, int* u) {
-  long best[3] = {-1, 0, 0};
-  for (int t = 64; t <= 1024; t += 64) {
-    for (int uu = 1; uu <= umax; ++uu) {
-      const long cover = (long)t * uu;
-      const long waste = (nvec + cover - 1) / cover * cover - nvec;
-      const long d = uu > upref ? uu - upref : upref - uu;
-      const bool better = best[0] < 0 || waste < best[0] ||
-                          (waste == best[0] && (d < best[1] || (d == best[1] && t > *threads)));
-      if (better) { best[0] = waste; best[1] = d; *threads = t; *u = uu; }
-    }
-  }
-}
 
 template <int U>
-void launch_dispatch_u(const moonep_sizes& s, const int32_t* dst, const uint16_t* x,
+void launch_dispatch_u(const moonep_sizes& s, const int32_t* dst, int nrows, const uint16_t* x,
                        uint16_t* recv, int nvec, int threads, hipStream_t st) {
   hipLaunchKernelGGL(dispatch_kernel<U>, dim3((unsigned)s.T), dim3(threads), 0, st, dst,
                      reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(recv), s.K,
-                     nvec, (int)s.recv_rows);
+                     nvec, nrows);
 }
 
 template <int KT, int U, bool WEIGHTED>
@@ -400,7 +459,7 @@ void launch_combine_ku(const moonep_sizes& s, const int32_t* dst, const float* w
                        const uint16_t* y, uint16_t* out, int nvec, int threads, hipStream_t st) {
   hipLaunchKernelGGL((combine_kernel<KT, U, WEIGHTED>), dim3((unsigned)s.T), dim3(threads), 0, st, dst,
                      w, reinterpret_cast<const u32x4*>(y), reinterpret_cast<u32x4*>(out), s.K,
-                     nvec, (int)s.recv_rows);
+                     nvec, dst ? (int)s.recv_rows : (int)s.A);
 }
 
 template <int KT, bool WEIGHTED>
@@ -417,32 +476,45 @@ void launch_combine_k(const moonep_sizes& s, const int32_t* dst, const float* w,
 
 }  // namespace
 
-hipError_t launch_dispatch(const moonep_sizes& s, const int32_t* plan, const uint16_t* x,
-                           int H, uint16_t* recv, hipStream_t st) {
+// rows from the plan's dst_row, or (staged) row t*K + k of a [T*K, H] staging buffer
+hipError_t dispatch_rows(const moonep_sizes& s, const int32_t* dst, int nrows, const uint16_t* x,
+                         int H, uint16_t* recv, hipStream_t st) {
   const int nvec = H / 8;
   int threads = 64, u = 1;
   row_shape(nvec, 8, 7, &threads, &u);
-  const int32_t* dst = plan + s.o_dst_row;
   switch (u) {
-    case 1: launch_dispatch_u<1>(s, dst, x, recv, nvec, threads, st); break;
-    case 2: launch_dispatch_u<2>(s, dst, x, recv, nvec, threads, st); break;
-    case 3: launch_dispatch_u<3>(s, dst, x, recv, nvec, threads, st); break;
-    case 4: launch_dispatch_u<4>(s, dst, x, recv, nvec, threads, st); break;
-    case 5: launch_dispatch_u<5>(s, dst, x, recv, nvec, threads, st); break;
-    case 6: launch_dispatch_u<6>(s, dst, x, recv, nvec, threads, st); break;
-    case 7: launch_dispatch_u<7>(s, dst, x, recv, nvec, threads, st); break;
-    default: launch_dispatch_u<8>(s, dst, x, recv, nvec, threads, st); break;
+    case 1: launch_dispatch_u<1>(s, dst, nrows, x, recv, nvec, threads, st); break;
+    case 2: launch_dispatch_u<2>(s, dst, nrows, x, recv, nvec, threads, st); break;
+    case 3: launch_dispatch_u<3>(s, dst, nrows, x, recv, nvec, threads, st); break;
+    case 4: launch_dispatch_u<4>(s, dst, nrows, x, recv, nvec, threads, st); break;
+    case 5: launch_dispatch_u<5>(s, dst, nrows, x, recv, nvec, threads, st); break;
+    case 6: launch_dispatch_u<6>(s, dst, nrows, x, recv, nvec, threads, st); break;
+    case 7: launch_dispatch_u<7>(s, dst, nrows, x, recv, nvec, threads, st); break;
+    default: launch_dispatch_u<8>(s, dst, nrows, x, recv, nvec, threads, st); break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch(const moonep_sizes& s, const int32_t* plan, const uint16_t* x,
+                           int H, uint16_t* recv, hipStream_t st) {
+  return dispatch_rows(s, plan + s.o_dst_row, (int)s.recv_rows, x, H, recv, st);
+}
+
+hipError_t launch_dispatch_staged(const moonep_sizes& s, const int32_t* plan, const uint16_t* x,
+                                  int H, uint16_t* stage, uint16_t* recv, hipStream_t st) {
+  const hipError_t err = dispatch_rows(s, nullptr, (int)s.A, x, H, stage, st);
+  if (err != hipSuccess) return err;
+  launch_copy_rows<true>(s, plan + s.o_dst_row, stage, recv, H / 8, st);
   return hipGetLastError();
 }
 
 template <bool WEIGHTED>
 hipError_t launch_gather_sum(const moonep_sizes& s, const int32_t* plan, const uint16_t* y,
-                             int H, uint16_t* out, hipStream_t st) {
+                             int H, uint16_t* out, hipStream_t st, bool staged = false) {
   const int nvec = H / 8;
   int threads = 64, u = 1;
   row_shape(nvec, 4, 2, &threads, &u);
-  const int32_t* dst = plan + s.o_dst_row;
+  const int32_t* dst = staged ? nullptr : plan + s.o_dst_row;
   const float* w = reinterpret_cast<const float*>(plan + s.o_w);
   switch (s.K) {
     case 1: launch_combine_k<1, WEIGHTED>(s, dst, w, y, out, nvec, threads, u, st); break;
@@ -458,6 +530,14 @@ hipError_t launch_gather_sum(const moonep_sizes& s, const int32_t* plan, const u
 hipError_t launch_combine(const moonep_sizes& s, const int32_t* plan, const uint16_t* y,
                           int H, uint16_t* out, hipStream_t st) {
   return launch_gather_sum<true>(s, plan, y, H, out, st);
+}
+
+hipError_t launch_combine_staged(const moonep_sizes& s, const int32_t* plan, const uint16_t* y,
+                                 int H, uint16_t* stage, uint16_t* out, hipStream_t st) {
+  launch_copy_rows<false>(s, plan + s.o_dst_row, y, stage, H / 8, st);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_gather_sum<true>(s, plan, stage, H, out, st, true);
 }
 
 hipError_t launch_dispatch_bwd(const moonep_sizes& s, const int32_t* plan, const uint16_t* g_recv,

@@ -62,6 +62,8 @@ def lib():
     L.moonep_reduce_grad.argtypes = [ctypes.POINTER(PlanDesc), vp, vp, i64, vp]
     L.moonep_dispatch_bwd.argtypes = [ctypes.POINTER(PlanDesc), vp, i32, vp, vp]
     L.moonep_combine_bwd.argtypes = [ctypes.POINTER(PlanDesc), vp, vp, i32, vp, vp, vp]
+    L.moonep_dispatch_staged.argtypes = [ctypes.POINTER(PlanDesc), vp, i32, vp, vp, vp]
+    L.moonep_combine_staged.argtypes = [ctypes.POINTER(PlanDesc), vp, i32, vp, vp, vp]
     L.moonep_prefetch_weight.argtypes = [ctypes.POINTER(PlanDesc), vp, i64, vp, vp]
     L.moonep_expert_stub.argtypes = [ctypes.POINTER(PlanDesc), vp, vp, vp, vp, i64, i32, vp, vp]
     L.moonep_plan_status.argtypes = [ctypes.POINTER(PlanDesc), ctypes.POINTER(PlanStats), vp]
@@ -69,7 +71,8 @@ def lib():
     L.moonep_strerror.restype = ctypes.c_char_p
     for f in ("moonep_query", "moonep_plan", "moonep_dispatch", "moonep_combine",
               "moonep_reduce_grad", "moonep_plan_status", "moonep_dispatch_bwd",
-              "moonep_combine_bwd", "moonep_prefetch_weight", "moonep_expert_stub"):
+              "moonep_combine_bwd", "moonep_prefetch_weight", "moonep_expert_stub",
+              "moonep_dispatch_staged", "moonep_combine_staged"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -78,7 +81,7 @@ def lib():
 EXPORTS = ("moonep_query", "moonep_plan", "moonep_dispatch", "moonep_combine",
            "moonep_reduce_grad", "moonep_plan_status", "moonep_strerror",
            "moonep_dispatch_bwd", "moonep_combine_bwd", "moonep_prefetch_weight",
-           "moonep_expert_stub")
+           "moonep_expert_stub", "moonep_dispatch_staged", "moonep_combine_staged")
 
 
 def _check(rc):
@@ -187,6 +190,38 @@ def moonep_combine(plan: Plan, y, out=None, stream=None):
         raise MoonepError("out must be [T, H]")
     _check(lib().moonep_combine(ctypes.byref(plan.desc), _dev(y, torch.bfloat16, "y"), H,
                                 _dev(out, torch.bfloat16, "out"), _stream(stream)))
+    return out
+
+
+def _stage(plan, H, stage, device):
+    if stage is None:
+        stage = torch.empty(plan.sz.A, H, dtype=torch.bfloat16, device=device)
+    if stage.numel() != plan.sz.A * H:
+        raise MoonepError("stage must be [T*K, H]")
+    return stage
+
+
+def moonep_dispatch_staged(plan: Plan, x, recv=None, stage=None, stream=None):
+    """Non-zero-copy dispatch: x -> stage (arrival order) -> recv (epilogue copy)."""
+    H = x.shape[-1]
+    stage = _stage(plan, H, stage, x.device)
+    if recv is None:
+        recv = torch.empty(plan.sz.recv_rows, H, dtype=torch.bfloat16, device=x.device)
+    _check(lib().moonep_dispatch_staged(ctypes.byref(plan.desc), _dev(x, torch.bfloat16, "x"), H,
+                                        _dev(stage, torch.bfloat16, "stage"),
+                                        _dev(recv, torch.bfloat16, "recv"), _stream(stream)))
+    return recv
+
+
+def moonep_combine_staged(plan: Plan, y, out=None, stage=None, stream=None):
+    """Non-zero-copy combine: y -> stage (prologue copy) -> weighted sum -> out."""
+    H = y.shape[-1]
+    stage = _stage(plan, H, stage, y.device)
+    if out is None:
+        out = torch.empty(plan.sz.T, H, dtype=torch.bfloat16, device=y.device)
+    _check(lib().moonep_combine_staged(ctypes.byref(plan.desc), _dev(y, torch.bfloat16, "y"), H,
+                                       _dev(stage, torch.bfloat16, "stage"),
+                                       _dev(out, torch.bfloat16, "out"), _stream(stream)))
     return out
 
 

@@ -135,6 +135,22 @@ int moonep_dispatch(const moonep_plan_desc* plan, const uint16_t* x, int H, uint
 int moonep_combine(const moonep_plan_desc* plan, const uint16_t* y, int H, uint16_t* out,
                    hipStream_t stream);
 
+/* Staged (non-zero-copy) dispatch, the A/B baseline for zero-copy ("MoonshotAI/MoonEP
+ * 딥다이브", section 2, point 2: the conventional scheme receives tokens into a
+ * communication buffer, then permutes and copies them into the user buffer; section 8,
+ * exercise D measures that copy):
+ *   stage[t*K + k, :] = x[t, :]                  (arrival order)
+ *   recv[dst_row[t,k], :] = stage[t*K + k, :]    (the epilogue copy)
+ * recv ends bit-identical to moonep_dispatch's.  stage: device bf16 [T*K, H]. */
+int moonep_dispatch_staged(const moonep_plan_desc* plan, const uint16_t* x, int H,
+                           uint16_t* stage, uint16_t* recv, hipStream_t stream);
+
+/* Staged combine (same passage): the prologue copy stage[t*K + k, :] = y[dst_row[t,k], :],
+ * then out[t] as in moonep_combine, read from the staging buffer.  out ends bit-identical
+ * to moonep_combine's.  stage: device bf16 [T*K, H]. */
+int moonep_combine_staged(const moonep_plan_desc* plan, const uint16_t* y, int H,
+                          uint16_t* stage, uint16_t* out, hipStream_t stream);
+
 /* Backward of dispatch, reusing the forward plan ("MoonshotAI/MoonEP 딥다이브", section 4,
  * design pattern 1: the plan serves both backward passes).  Dispatch copied x[t] into
  * its K rows, so
