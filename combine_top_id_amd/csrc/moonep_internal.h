@@ -4,6 +4,7 @@
 #pragma once
 
 #include <stdint.h>
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include "moonep.h"
@@ -16,7 +17,7 @@ constexpr int kMapWaves = 8;                // waves per workgroup of the hist/m
 constexpr int kMapThreads = kMapWaves * 64;
 constexpr int kPlanThreads = 1024;          // the single planner workgroup
 constexpr int kPieceInts = 8;               // e, r, slot, cnt, start, fbpos, row0, pad
-constexpr int kMaxBlocks = 64;              // target number of assignment blocks
+constexpr int kColumnBudget = 32768;        // blocks x experts the planner scans in registers
 
 // header words
 enum Hdr : int {
@@ -50,10 +51,11 @@ inline int fill_sizes(int R, int E, int K, int S, int slots, moonep_sizes* s) {
   s->T = T; s->A = A;
   s->recv_rows = NvS * R;
   // assignment blocks: kMapThreads * m assignments each, m a power of two in [1, 32],
-  // aiming at no more than kMaxBlocks blocks so the planner's per-expert block prefix
-  // stays one batch of loads per thread.
+  // aiming at no more than 32768 / E blocks: the planner then scans at most 32 block
+  // counts per thread (1024 threads, E columns), held in registers.
+  const int64_t target = std::max<int64_t>(1, kColumnBudget / E);
   int64_t m = 1;
-  while (m < 32 && (int64_t)kMapThreads * m * kMaxBlocks < A) m *= 2;
+  while (m < 32 && (int64_t)kMapThreads * m * target < A) m *= 2;
   s->blk = (int32_t)(kMapThreads * m);
   s->nblk = (int32_t)((A + s->blk - 1) / s->blk);
   int64_t o = 0;

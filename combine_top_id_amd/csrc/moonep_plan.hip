@@ -155,7 +155,6 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
   // ws[b][e] holds block b's count of expert e.  Each column is split into `tpc` segments
   // of consecutive blocks, one thread per (segment, expert): segment sums, then the
   // exclusive scan over blocks, kept in registers and written back at the very end.
-  if (tid < 64) hl_s[tid] = 0;
   if (tid == 0) { bad_s = INT_MAX; maxload_s = 0; err_s = 0; }
   const int nblk = s.nblk;
   int tpc = 1;
@@ -191,14 +190,23 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
   __syncthreads();
   if (mybad != INT_MAX) atomicMin(&bad_s, mybad);
   int colbase = 0;   // the column thread's first base (blocks before b0)
+  int mytotal = 0;
   if (col_thread) {
     for (int g = 0; g < cg; ++g) colbase += part_s[g * E + ce];
     if (cg == tpc - 1) {
-      const int total = colbase + part_s[cg * E + ce];
-      load_s[ce] = total;
-      atomicAdd(&hl_s[ce / E_loc], total);
-      atomicMax(&maxload_s, total);
+      mytotal = colbase + part_s[cg * E + ce];
+      load_s[ce] = mytotal;
     }
+  }
+  for (int off = 32; off >= 1; off >>= 1) mytotal = max(mytotal, __shfl_xor(mytotal, off, 64));
+  if (lane == 0 && mytotal > 0) atomicMax(&maxload_s, mytotal);
+  __syncthreads();
+  if (tid < R) {
+    // home load of rank tid (independent LDS reads, unrolled)
+    int hl = 0;
+#pragma unroll 8
+    for (int g = 0; g < E_loc; ++g) hl += load_s[tid * E_loc + g];
+    hl_s[tid] = hl;
   }
   __syncthreads();
 
@@ -285,10 +293,19 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
     int used = 0, fbrows = 0, nfb = 0;
     int np = 0;
     bool err = false;
-    for (int q = 0; q < nshed; ++q) {
-      const int e = order_s[q];
-      int rem = shed_s[e];
-      int start = keep_s[e];
+    // 64 experts at a time sit in lane registers; each iteration broadcasts its expert's
+    // id, shed and keep counts with readlane, so the inner loop only stores to LDS and
+    // never waits on it
+    for (int q0 = 0; q0 < nshed; q0 += 64) {
+     const int qq = q0 + lane;
+     const int q_e = qq < nshed ? order_s[qq] : 0;
+     const int q_shed = qq < nshed ? shed_s[q_e] : 0;
+     const int q_keep = qq < nshed ? keep_s[q_e] : 0;
+     const int qn = min(64, nshed - q0);
+     for (int qi = 0; qi < qn; ++qi) {
+      const int e = __builtin_amdgcn_readlane(q_e, qi);
+      int rem = __builtin_amdgcn_readlane(q_shed, qi);
+      int start = __builtin_amdgcn_readlane(q_keep, qi);
       const int first = np;
       {
         const bool elig = lane < R && D > 0 && used < slots;
@@ -341,6 +358,7 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
         pnum_s[e] = np - first;
       }
       err = err || rem != 0;
+     }
     }
     used_s[lane] = used;
     fb_s[lane] = fbrows;
