@@ -55,6 +55,16 @@ __device__ __forceinline__ int lane63(int v) { return __builtin_amdgcn_readlane(
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+// Number of entries of the ascending array a[0, n) that are <= x.
+__device__ __forceinline__ int count_le(const int32_t* a, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] <= x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
 __device__ __forceinline__ int align_rows(int n) { return (n + kRowAlign - 1) / kRowAlign * kRowAlign; }
 
 // ---------------------------------------------------------------------------------------
@@ -134,16 +144,16 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
   int32_t* pfirst_s = list_s + E;   // [E]
   int32_t* pnum_s = pfirst_s + E;   // [E]
   int32_t* pe_s = pnum_s + E;             // pieces: expert, rank, slot, count, start,
-  int32_t* pr_s = pe_s + PM;              //   fallback position, first row   [P_max] each
+  int32_t* pr_s = pe_s + PM;              //   [P_max] each
   int32_t* psl_s = pr_s + PM;
   int32_t* pc_s = psl_s + PM;
   int32_t* pst_s = pc_s + PM;
-  int32_t* pfb_s = pst_s + PM;
-  int32_t* prow_s = pfb_s + PM;
+  int32_t* prel_s = pst_s + PM;           //   row inside its slot or fallback region
+  int32_t* qbase_s = prel_s + PM;         // [nshed] fast placement's per-expert base
   int32_t* home_s = list_s;         // [E] home group rows, after the ordering is done
   int32_t* part_s = pe_s;           // [kPlanThreads] column segment sums, used before the
                                     // pieces exist
-  __shared__ int32_t hl_s[64], used_s[64], fb_s[64], nfb_s[64];
+  __shared__ int32_t hl_s[64], used_s[64], fb_s[64], nfb_s[64], sr_s[64], ht_s[64], dend_s[64];
   __shared__ int bad_s, nshed_s, npieces_s, maxload_s, err_s;
 
   int32_t* hdr = plan + s.o_hdr;
@@ -289,14 +299,86 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
     // fills its receiver except possibly the last); any rest goes, again in id order, to
     // ranks that are short but have no free slot (fallback pieces).  This is the
     // one-assignment-at-a-time greedy, done one expert at a time.
-    int D = lane < R ? max(0, C - hl_s[lane]) : 0;
-    int used = 0, fbrows = 0, nfb = 0;
-    int np = 0;
-    bool err = false;
-    // 64 experts at a time sit in lane registers; each iteration broadcasts its expert's
-    // id, shed and keep counts with readlane, so the inner loop only stores to LDS and
-    // never waits on it
+    //
+    // Fast path.  Without a slot budget the greedy simply cuts the shed stream (the
+    // shedding experts' assignments laid end to end in plan order, positions [0, tot)) at
+    // the boundaries of the ranks' deficit ranges (short ranks laid end to end in id
+    // order): piece (q, r) is the overlap of expert q's range with rank r's.  Run in step
+    // with the budgeted greedy, the two agree on every expert before the first one that
+    // would give some rank its (slots+1)-th piece.  That prefix is placed by the cut, in
+    // parallel over ranks, and the one-expert-at-a-time loop carries on from there.
+    const int D0 = lane < R ? max(0, C - hl_s[lane]) : 0;
+    const int dend = wave_incl_scan(D0);            // rank lane's deficit range [dbeg, dend)
+    const int dbeg = dend - D0;
+    const int dtot = lane63(dend);
+    const uint64_t mD = __ballot(D0 > 0);
+    const int posr = __popcll(mD & lt);             // short ranks before lane
+    dend_s[lane] = dend;
+    int32_t* sq_s = list_s;     // [nshed] first stream position of expert q (list_s is free)
+    int32_t* qb_s = qbase_s;    // [nshed] piece index of expert q's first piece minus the
+                                //   short-rank position of its first receiver
+    int tot = 0;
     for (int q0 = 0; q0 < nshed; q0 += 64) {
+      const int q = q0 + lane;
+      const int sh = q < nshed ? shed_s[order_s[q]] : 0;
+      const int incl = wave_incl_scan(sh);
+      if (q < nshed) sq_s[q] = tot + incl - sh;
+      tot += lane63(incl);
+    }
+    int np = 0;
+    bool ok = tot <= dtot;      // always true when every rank's quota is S*K
+    for (int q0 = 0; q0 < nshed && ok; q0 += 64) {
+      const int q = q0 + lane;
+      int n = 0, lo = 0;
+      if (q < nshed) {
+        const int x0 = sq_s[q];
+        const int x1 = (q + 1 < nshed ? sq_s[q + 1] : tot) - 1;   // last position
+        lo = count_le(dend_s, R, x0);               // receiving ranks: lo .. hi
+        const int hi = count_le(dend_s, R, x1);
+        const uint64_t upto = hi >= 63 ? ~0ull : ((2ull << hi) - 1);
+        n = __popcll(mD & upto & ~((1ull << lo) - 1));
+      }
+      const int incl = wave_incl_scan(n);
+      if (q < nshed) {
+        const int e = order_s[q];
+        pfirst_s[e] = np + incl - n;
+        pnum_s[e] = n;
+        qb_s[q] = np + incl - n - __popcll(mD & ((1ull << lo) - 1));
+      }
+      np += lane63(incl);
+    }
+    const bool gets = lane < R && D0 > 0 && dbeg < tot;
+    const int hi_pos = min(dend, tot);
+    const int qf = gets ? count_le(sq_s, nshed, dbeg) - 1 : 0;
+    const int ql = gets ? count_le(sq_s, nshed, hi_pos - 1) - 1 : -1;
+    // first expert that would overfill some rank's slots (nshed when none would)
+    int qstar = gets && ql - qf + 1 > slots ? qf + slots : nshed;
+    for (int d = 32; d >= 1; d >>= 1) qstar = min(qstar, __shfl_xor(qstar, d, 64));
+    if (!ok || np > PM) qstar = 0;
+
+    int D = D0, used = 0, fbrows = 0, nfb = 0, slotrows = 0;
+    bool err = false;
+    {
+      const int qe = min(ql, qstar - 1);
+      for (int q = qf; q <= qe; ++q) {     // this rank's pieces of the prefix, <= slots
+        const int e = order_s[q];
+        const int s0 = sq_s[q];
+        const int s1 = q + 1 < nshed ? sq_s[q + 1] : tot;
+        const int x = max(dbeg, s0);
+        const int take = min(dend, s1) - x;
+        const int p = qb_s[q] + posr;
+        pe_s[p] = e; pr_s[p] = lane; psl_s[p] = q - qf; pc_s[p] = take;
+        pst_s[p] = keep_s[e] + (x - s0); prel_s[p] = slotrows;
+        slotrows += align_rows(take);
+        used += 1;
+      }
+      const int send = qstar < nshed ? sq_s[qstar] : tot;   // end of the prefix's stream
+      if (lane < R && D0 > 0 && dbeg < send) D -= min(dend, send) - dbeg;
+      np = qstar == 0 ? 0 : (qstar < nshed ? pfirst_s[order_s[qstar]] : np);
+    }
+    // 64 experts at a time sit in lane registers; each iteration broadcasts its expert's
+    // id, shed and keep counts with readlane, so the inner loop only stores to LDS
+    for (int q0 = qstar; q0 < nshed; q0 += 64) {
      const int qq = q0 + lane;
      const int q_e = qq < nshed ? order_s[qq] : 0;
      const int q_shed = qq < nshed ? shed_s[q_e] : 0;
@@ -318,11 +400,12 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
           const int p = np + __popcll(m & lt);
           if (p < PM) {
             pe_s[p] = e; pr_s[p] = lane; psl_s[p] = used; pc_s[p] = take;
-            pst_s[p] = start + excl; pfb_s[p] = 0;
+            pst_s[p] = start + excl; prel_s[p] = slotrows;
           } else {
             err = true;
           }
           used += 1;
+          slotrows += align_rows(take);
           D -= take;
         }
         const int moved = min(rem, lane63(incl));
@@ -340,7 +423,7 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
           const int p = np + __popcll(m & lt);
           if (p < PM) {
             pe_s[p] = e; pr_s[p] = lane; psl_s[p] = -1; pc_s[p] = take;
-            pst_s[p] = start + excl; pfb_s[p] = fbrows;
+            pst_s[p] = start + excl; prel_s[p] = fbrows;
           } else {
             err = true;
           }
@@ -363,6 +446,7 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
     used_s[lane] = used;
     fb_s[lane] = fbrows;
     nfb_s[lane] = nfb;
+    sr_s[lane] = slotrows;
     if (__ballot(err || (lane < R && D != 0))) { if (lane == 0) err_s = 1; }
     if (lane == 0) { npieces_s = min(np, PM); nshed_s = nshed; }
   }
@@ -371,7 +455,7 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
   // ---- layout of each rank's buffer, one wave per rank --------------------------------------
   // Home groups, then slot groups (slot order = the order the rank's slot pieces were
   // created), then the fallback region; each home and slot group starts on a multiple of
-  // ROW_ALIGN rows.  The same scans give every piece its first row.
+  // ROW_ALIGN rows.  Slot groups' offsets inside the slot region were fixed while placing.
   const int np = npieces_s;
   int32_t* off = plan + s.o_off;
   int32_t* slot_expert = plan + s.o_slot_expert;
@@ -388,43 +472,33 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
       }
       carry += lane63(incl);
     }
-    for (int p0 = 0; p0 < np; p0 += 64) {          // slot pieces of rank r
-      const int p = p0 + lane;
-      const bool mine = p < np && pr_s[p] == r && psl_s[p] >= 0;
-      const int a = mine ? align_rows(pc_s[p]) : 0;
-      const int incl = wave_incl_scan(a);
-      if (mine) {
-        const int row = carry + incl - a;
-        o[E_loc + psl_s[p]] = row;
-        slot_expert[r * slots + psl_s[p]] = pe_s[p];
-        prow_s[p] = r * NvS + row;
-      }
-      carry += lane63(incl);
-    }
+    const int srows = sr_s[r];
     for (int sl = used_s[r] + lane; sl < slots; sl += 64) {   // unused slots
-      o[E_loc + sl] = carry;
+      o[E_loc + sl] = carry + srows;
       slot_expert[r * slots + sl] = -1;
     }
     if (lane == 0) {
-      o[G] = carry;
-      if (carry + fb_s[r] > NvS) err_s = 1;
-    }
-    for (int p0 = 0; p0 < np; p0 += 64) {          // fallback pieces of rank r
-      const int p = p0 + lane;
-      if (p < np && pr_s[p] == r && psl_s[p] < 0) prow_s[p] = r * NvS + carry + pfb_s[p];
+      ht_s[r] = carry;
+      o[G] = carry + srows;
+      if (carry + srows + fb_s[r] > NvS) err_s = 1;
     }
   }
   __syncthreads();
 
   // ---- write the plan ---------------------------------------------------------------------
   for (int p = tid; p < np; p += kPlanThreads) {
+    const int r = pr_s[p], sl = psl_s[p], rel = prel_s[p];
+    const int rowin = ht_s[r] + (sl >= 0 ? rel : sr_s[r] + rel);   // row inside rank r
+    const int row0 = r * NvS + rowin;
+    if (sl >= 0) {
+      off[(int64_t)r * (G + 1) + E_loc + sl] = rowin;
+      slot_expert[r * slots + sl] = pe_s[p];
+    }
     int32_t* pc = plan + s.o_pieces + (int64_t)p * kPieceInts;
-    pc[P_E] = pe_s[p]; pc[P_R] = pr_s[p]; pc[P_SLOT] = psl_s[p]; pc[P_CNT] = pc_s[p];
-    pc[P_START] = pst_s[p]; pc[P_FBPOS] = pfb_s[p]; pc[P_ROW0] = prow_s[p]; pc[7] = 0;
-  }
-  for (int p = tid; p < np; p += kPlanThreads) {
+    pc[P_E] = pe_s[p]; pc[P_R] = r; pc[P_SLOT] = sl; pc[P_CNT] = pc_s[p];
+    pc[P_START] = pst_s[p]; pc[P_FBPOS] = sl >= 0 ? 0 : rel; pc[P_ROW0] = row0; pc[7] = 0;
     // packed (start, count, first row) for the map kernel
-    reinterpret_cast<i32x4*>(plan + s.o_ptab)[p] = i32x4{pst_s[p], pc_s[p], prow_s[p], 0};
+    reinterpret_cast<i32x4*>(plan + s.o_ptab)[p] = i32x4{pst_s[p], pc_s[p], row0, 0};
   }
   for (int e = tid; e < E; e += kPlanThreads) {
     plan[s.o_load + e] = load_s[e];

@@ -127,6 +127,51 @@ def test_random_cases(R, E, K, S, slots, H, mv):
     full_case(R, E, K, S, slots, H, ids.numpy(), wt.numpy(), seed, G_el=8 if slots else 0)
 
 
+def _cut_prefix(p):
+    """For coverage only: how many shedding experts (in plan order) come before the first
+    one that, were there no slot budget, would give some rank more than `slots` pieces.
+    The planner places that prefix in parallel and the rest one expert at a time."""
+    sz = p.sz
+    order = [int(e) for e in p.order if p.shed[e] > 0]
+    ends = np.cumsum([int(p.shed[e]) for e in order])
+    starts = ends - np.array([int(p.shed[e]) for e in order])
+    dend = np.cumsum(p.deficit)
+    dbeg = dend - p.deficit
+    first_bad = len(order)
+    for r in range(sz.R):
+        if p.deficit[r] == 0:
+            continue
+        hit = [q for q in range(len(order)) if starts[q] < dend[r] and ends[q] > dbeg[r]]
+        if len(hit) > sz.slots:
+            first_bad = min(first_bad, hit[sz.slots])
+    return first_bad, len(order)
+
+
+def test_tight_slot_budgets():
+    """Plans under small slot budgets and strong skew, where placement switches from the
+    parallel cut to one expert at a time part way through the shedding experts."""
+    rng = np.random.default_rng(4321)
+    kinds = set()
+    for i in range(32):
+        R = int(rng.choice([2, 3, 4, 7, 8, 16, 32, 64]))
+        E = R * int(rng.choice([1, 2, 3, 4, 6]))
+        K = int(rng.integers(1, min(E, 8) + 1))
+        S = int(rng.integers(4, 200))
+        slots = int(rng.choice([1, 2, 3, 4]))
+        mv = float(rng.choice([0.5, 1.0, 3.0, 8.0, 20.0]))
+        seed = 9000 + i
+        say(f"tight slots case {i}: R={R} E={E} K={K} S={S} slots={slots} maxvio={mv}")
+        ids, wt, _, _ = make_routing(R, E, K, S, mv, seed)
+        ids_np = ids.numpy()
+        plan = M.moonep_plan(*to_dev_ids(ids_np, wt.numpy()), R, E, K, S, slots)
+        p = O.plan(ids_np, R, E, K, S, slots)
+        assert_plan_matches(read_plan(plan), p, O.slot_map(p, ids_np))
+        q, n = _cut_prefix(p)
+        kinds.add("none" if n == 0 else ("all" if q == n else ("part" if q > 0 else "zero")))
+    torch.cuda.synchronize()
+    assert "part" in kinds and "all" in kinds, kinds
+
+
 def test_balanced_routing_has_no_pieces():
     R, E, K, S = 8, 64, 8, 128
     ids, wt = make_balanced_routing(R, E, K, S)
