@@ -153,7 +153,8 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
   int32_t* home_s = list_s;         // [E] home group rows, after the ordering is done
   int32_t* part_s = pe_s;           // [kPlanThreads] column segment sums, used before the
                                     // pieces exist
-  __shared__ int32_t hl_s[64], used_s[64], fb_s[64], nfb_s[64], sr_s[64], ht_s[64], dend_s[64];
+  __shared__ int32_t hl_s[64], used_s[64], fb_s[64], nfb_s[64], sr_s[64], ht_s[64], dend_s[64],
+      xs_s[64], wtot_s[kPlanThreads / 64];
   __shared__ int bad_s, nshed_s, npieces_s, maxload_s, err_s;
 
   int32_t* hdr = plan + s.o_hdr;
@@ -452,35 +453,37 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
   }
   __syncthreads();
 
-  // ---- layout of each rank's buffer, one wave per rank --------------------------------------
+  // ---- layout of each rank's buffer -----------------------------------------------------
   // Home groups, then slot groups (slot order = the order the rank's slot pieces were
   // created), then the fallback region; each home and slot group starts on a multiple of
-  // ROW_ALIGN rows.  Slot groups' offsets inside the slot region were fixed while placing.
+  // ROW_ALIGN rows.  Slot and fallback rows were fixed relative to their regions while
+  // placing.  Home offsets: one exclusive scan over all experts (thread = expert), minus
+  // the scan's value at the rank's first expert.
   const int np = npieces_s;
   int32_t* off = plan + s.o_off;
   int32_t* slot_expert = plan + s.o_slot_expert;
-  for (int r = wave; r < R; r += kPlanWaves) {
-    int32_t* o = off + (int64_t)r * (G + 1);
-    int carry = 0;
-    for (int g0 = 0; g0 < E_loc; g0 += 64) {
-      const int g = g0 + lane;
-      const int a = g < E_loc ? align_rows(keep_s[r * E_loc + g]) : 0;
-      const int incl = wave_incl_scan(a);
-      if (g < E_loc) {
-        o[g] = carry + incl - a;
-        home_s[r * E_loc + g] = r * NvS + carry + incl - a;
+  {
+    const int e = tid;
+    const int a = e < E ? align_rows(keep_s[e]) : 0;
+    const int incl = wave_incl_scan(a);
+    if (lane == 63) wtot_s[wave] = incl;
+    __syncthreads();
+    int pre = 0;
+    for (int v = 0; v < wave; ++v) pre += wtot_s[v];
+    const int X = pre + incl - a;           // exclusive scan over experts
+    const int r = e / E_loc, g = e - r * E_loc;
+    if (e < E && g == 0) xs_s[r] = X;
+    __syncthreads();
+    if (e < E) {
+      const int o_in = X - xs_s[r];
+      off[(int64_t)r * (G + 1) + g] = o_in;
+      home_s[e] = r * NvS + o_in;
+      if (g == E_loc - 1) {
+        const int ht = o_in + a;
+        ht_s[r] = ht;
+        off[(int64_t)r * (G + 1) + G] = ht + sr_s[r];
+        if (ht + sr_s[r] + fb_s[r] > NvS) err_s = 1;
       }
-      carry += lane63(incl);
-    }
-    const int srows = sr_s[r];
-    for (int sl = used_s[r] + lane; sl < slots; sl += 64) {   // unused slots
-      o[E_loc + sl] = carry + srows;
-      slot_expert[r * slots + sl] = -1;
-    }
-    if (lane == 0) {
-      ht_s[r] = carry;
-      o[G] = carry + srows;
-      if (carry + srows + fb_s[r] > NvS) err_s = 1;
     }
   }
   __syncthreads();
@@ -499,6 +502,13 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
     pc[P_START] = pst_s[p]; pc[P_FBPOS] = sl >= 0 ? 0 : rel; pc[P_ROW0] = row0; pc[7] = 0;
     // packed (start, count, first row) for the map kernel
     reinterpret_cast<i32x4*>(plan + s.o_ptab)[p] = i32x4{pst_s[p], pc_s[p], row0, 0};
+  }
+  for (int i = tid; i < R * slots; i += kPlanThreads) {   // unused slots
+    const int r = i / slots, sl = i - r * slots;
+    if (sl >= used_s[r]) {
+      off[(int64_t)r * (G + 1) + E_loc + sl] = ht_s[r] + sr_s[r];
+      slot_expert[i] = -1;
+    }
   }
   for (int e = tid; e < E; e += kPlanThreads) {
     plan[s.o_load + e] = load_s[e];
