@@ -18,6 +18,7 @@ constexpr int kMapThreads = kMapWaves * 64;
 constexpr int kPlanThreads = 1024;          // the single planner workgroup
 constexpr int kPieceInts = 8;               // e, r, slot, cnt, start, fbpos, row0, pad
 constexpr int kColumnBudget = 32768;        // blocks x experts the planner scans in registers
+constexpr int kMapChunks = 8;               // 64-assignment chunks per map wave, at most
 
 // header words
 enum Hdr : int {
@@ -77,15 +78,31 @@ inline int fill_sizes(int R, int E, int K, int S, int slots, moonep_sizes* s) {
   s->plan_bytes = o * 4;
   // workspace: per-block expert counts [nblk][E] (overwritten by the planner with
   // per-block bases), per-block first bad index [nblk], per-wave prefixes inside each
-  // block [nblk][kMapWaves][E]
+  // block [nblk][kMapWaves][E], and, when a histogram wave's 64*m assignments are split
+  // into Q > 1 map sub-blocks, the wave's running counts at each inner sub-block boundary
+  // [nblk][kMapWaves][Q-1][E]
+  const int64_t Q = m > kMapChunks ? m / kMapChunks : 1;
   s->workspace_bytes = (align64((int64_t)s->nblk * E) + align64(s->nblk) +
-                        align64((int64_t)s->nblk * kMapWaves * E)) * 4;
+                        align64((int64_t)s->nblk * kMapWaves * E) +
+                        align64((int64_t)s->nblk * kMapWaves * (Q - 1) * E)) * 4;
   return MOONEP_OK;
+}
+
+// chunks per map wave and map sub-blocks per histogram wave
+__host__ __device__ inline int map_chunks(const moonep_sizes& s) {
+  const int m = s.blk / kMapThreads;
+  return m < kMapChunks ? m : kMapChunks;
+}
+__host__ __device__ inline int map_split(const moonep_sizes& s) {
+  return s.blk / kMapThreads / map_chunks(s);
 }
 
 // workspace offsets (int32 elements)
 __host__ __device__ inline int64_t ws_bad(const moonep_sizes& s) { return align64((int64_t)s.nblk * s.E); }
 __host__ __device__ inline int64_t ws_sub(const moonep_sizes& s) { return ws_bad(s) + align64(s.nblk); }
+__host__ __device__ inline int64_t ws_snap(const moonep_sizes& s) {
+  return ws_sub(s) + align64((int64_t)s.nblk * kMapWaves * s.E);
+}
 
 // Launchers (defined in the .hip files).
 hipError_t launch_plan(const moonep_sizes& s, const int32_t* ids, const float* w,

@@ -18,7 +18,9 @@
 //                      greedy placement (one wave, lane r = rank r), buffer layout
 //                      (one wave per rank), piece rows, statistics.  Everything stays in
 //                      LDS until one final write of the plan.
-//   3. map_kernel      one single-wave workgroup per sub-block: the stable rank j of each
+//   3. map_kernel      one single-wave workgroup per map sub-block (a histogram wave's
+//                      sub-block, or a part of at most 8 chunks of it, whose starting
+//                      counts the histogram wave recorded): the stable rank j of each
 //                      assignment among its expert's assignments (ballot peer masks and an
 //                      LDS counter per expert), then its row; copies the top-K weights.
 #include <climits>
@@ -90,8 +92,18 @@ __global__ __launch_bounds__(kMapThreads) void hist_kernel(const int32_t* __rest
   if (tid == 0) bad = INT_MAX;
   __syncthreads();
   int mybad = INT_MAX;
+  // Q > 1: the map splits this wave's chunks into Q sub-blocks of MC chunks, and needs
+  // the wave's running counts at each inner boundary (one wave's LDS operations take
+  // effect in program order, so the reads see every earlier add of the wave)
+  constexpr int MC = M < kMapChunks ? M : kMapChunks;
+  constexpr int Q = M / MC;
+  int32_t* snap = ws + ws_snap(s) + ((int64_t)blockIdx.x * kMapWaves + wave) * (Q - 1) * E;
 #pragma unroll
   for (int c = 0; c < M; ++c) {
+    if (Q > 1 && c > 0 && c % MC == 0) {
+      int32_t* sn = snap + (int64_t)(c / MC - 1) * E;
+      for (int e = lane; e < E; e += 64) sn[e] = mine[e];
+    }
     const int64_t i = i_wave + c * 64 + lane;
     if (i < s.A) {
       const int id = idv[c];
@@ -599,10 +611,12 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
 // 3. token -> row map
 // ---------------------------------------------------------------------------------------
 
-// One single-wave workgroup per sub-block of 64*M assignments (wave w of block b in the
-// histogram's numbering).  Every global load it needs is issued first: ids, weights,
-// the per-expert tables, the sub-block's base per expert (block base from the planner +
-// earlier waves of the block from the histogram), the piece table.
+// One single-wave workgroup per map sub-block of 64*M assignments: part q of wave w of
+// block b in the histogram's numbering (a histogram wave with more than kMapChunks chunks
+// is split into Q parts).  Every global load it needs is issued first: ids, weights, the
+// per-expert tables, the sub-block's base per expert (block base from the planner +
+// earlier waves of the block + the wave's own earlier parts, both from the histogram),
+// the piece table.
 constexpr int kTab = 8;   // table entries per lane loaded per round trip
 
 template <int M> struct MapGroup { static constexpr int value = M < 8 ? M : 8; };
@@ -619,12 +633,16 @@ __global__ __launch_bounds__(64) void map_kernel(const int32_t* __restrict__ ids
   i32x4* xtab_s = lds4;                            // [E] keep, home row, first piece, count
   i32x4* ptab_s = xtab_s + E;                      // [P] start, count, first row
   int32_t* run = reinterpret_cast<int32_t*>(ptab_s + P);   // [E] running count per expert
+  uint64_t* mask_s = reinterpret_cast<uint64_t*>(run + ((E + 1) & ~1));   // [E+1] lanes per id
 
   constexpr int kMapGroup = MapGroup<M>::value;   // chunks ranked per pass
   const int lane = threadIdx.x;
-  const int b = blockIdx.x / kMapWaves, sw = blockIdx.x % kMapWaves;
+  const int Q = map_split(s);                     // map sub-blocks per histogram wave
+  const int per_blk = kMapWaves * Q;
+  const int b = blockIdx.x / per_blk, sb = blockIdx.x % per_blk;
+  const int sw = sb / Q, q = sb - sw * Q;         // histogram wave, part of it
   const int64_t A = s.A;
-  const int64_t i_wave = (int64_t)b * s.blk + (int64_t)sw * (64 * M);
+  const int64_t i_wave = (int64_t)b * s.blk + (int64_t)sb * (64 * M);
   int32_t* dst = plan + s.o_dst_row;
   float* wout = reinterpret_cast<float*>(plan + s.o_w);
   if (i_wave >= A) return;
@@ -644,11 +662,16 @@ __global__ __launch_bounds__(64) void map_kernel(const int32_t* __restrict__ ids
   const i32x4* ptab = reinterpret_cast<const i32x4*>(plan + s.o_ptab);
   const int32_t* bbase = ws + (int64_t)b * E;
   const int32_t* wbase = ws + ws_sub(s) + ((int64_t)b * kMapWaves + sw) * E;
+  // running count of the histogram wave before this part (none for its first part: the
+  // pointer then stays valid and the value is multiplied by 0)
+  const int32_t* qbase = q > 0 ? ws + ws_snap(s) + (((int64_t)b * kMapWaves + sw) * (Q - 1) + q - 1) * E
+                               : wbase;
+  const int qon = q > 0 ? 1 : 0;
   // loads use clamped (always valid) indices so that they stay unconditional and the
   // values stay in registers; only the LDS stores are guarded
   for (int e0 = 0; e0 < E || e0 < P; e0 += 64 * kTab) {
     i32x4 xt[kTab], pt[kTab];
-    int bb[kTab], wb[kTab];
+    int bb[kTab], wb[kTab], qb[kTab];
 #pragma unroll
     for (int k = 0; k < kTab; ++k) {
       const int e = e0 + k * 64 + lane;
@@ -656,15 +679,17 @@ __global__ __launch_bounds__(64) void map_kernel(const int32_t* __restrict__ ids
       xt[k] = xtab[ec];
       bb[k] = bbase[ec];
       wb[k] = wbase[ec];
+      qb[k] = qbase[ec];
       pt[k] = ptab[pc];
     }
 #pragma unroll
     for (int k = 0; k < kTab; ++k) {
       const int e = e0 + k * 64 + lane;
-      if (e < E) { xtab_s[e] = xt[k]; run[e] = bb[k] + wb[k]; }
+      if (e < E) { xtab_s[e] = xt[k]; run[e] = bb[k] + wb[k] + qon * qb[k]; }
       if (e < P) ptab_s[e] = pt[k];
     }
   }
+  for (int e = lane; e <= E; e += 64) mask_s[e] = 0;
   if (status != 0) {
     // invalid plan: map nothing
 #pragma unroll
@@ -677,25 +702,25 @@ __global__ __launch_bounds__(64) void map_kernel(const int32_t* __restrict__ ids
   // One wave: its LDS accesses are performed in program order, so no barrier is needed.
   //
   // Stable rank of each assignment among its expert's assignments, chunk by chunk (64
-  // assignments, lane order = i order): `below` = lanes of the chunk with the same id
-  // and a lower lane (ballot peer masks, one ballot per id bit); the group's lowest lane
-  // adds the group size to the expert's LDS counter and gets the count of all earlier
-  // chunks back (atomics of one wave are applied in issue order, so they are issued
-  // back to back without waiting), then hands it to its peers with a lane shuffle.
-  const int nbits = 32 - __clz(E);
+  // assignments, lane order = i order).  Peers (lanes of the chunk with the same id): each
+  // lane ORs its bit into mask[id], reads mask[id] back, and clears it, three LDS
+  // operations that take effect in that order for the whole wave, so the read sees exactly
+  // the chunk's lanes and the next chunk starts from zeros.  `below` = peers in lower
+  // lanes; the group's lowest lane adds the group size to the expert's LDS counter and
+  // gets the count of all earlier chunks back (atomics of one wave are applied in issue
+  // order, so they are issued back to back without waiting), then hands it to its peers
+  // with a lane shuffle.
   const uint64_t lt = lanemask_lt();
+  const uint64_t mybit = 1ull << lane;
   for (int c0 = 0; c0 < M; c0 += kMapGroup) {
-    // peer masks of kMapGroup chunks at once (independent chains, one ballot per id bit)
     uint64_t peers[kMapGroup];
 #pragma unroll
-    for (int u = 0; u < kMapGroup; ++u) peers[u] = ~0ull;
-    for (int bit = 0; bit < nbits; ++bit) {
-#pragma unroll
-      for (int u = 0; u < kMapGroup; ++u) {
-        const bool on = (idv[c0 + u] >> bit) & 1;
-        const uint64_t bl = __ballot(on);
-        peers[u] &= on ? bl : ~bl;
-      }
+    for (int u = 0; u < kMapGroup; ++u) {
+      // lanes past the end share the spare slot E
+      uint64_t* m = mask_s + min((unsigned)idv[c0 + u], (unsigned)E);
+      __hip_atomic_fetch_or(m, mybit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      peers[u] = __hip_atomic_load(m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_store(m, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     int below[kMapGroup], base[kMapGroup];
 #pragma unroll
@@ -723,9 +748,21 @@ __global__ __launch_bounds__(64) void map_kernel(const int32_t* __restrict__ ids
         if (j[u] < xt[u].x) {
           row = xt[u].y + j[u];
         } else {
-          for (int q = xt[u].z; q < xt[u].z + xt[u].w; ++q) {
-            const i32x4 pt = ptab_s[q];      // start, count, first row
-            if (j[u] < pt.x + pt.y) { row = pt.z + (j[u] - pt.x); break; }
+          // the expert's pieces cover [keep, load) in order: j falls in the last piece
+          // whose start is <= j.  Eight starts are read per LDS round trip.
+          const int pf = xt[u].z, pn = xt[u].w;
+          const int32_t* pstart = reinterpret_cast<const int32_t*>(ptab_s + pf);
+          int n_le = 0;
+          for (int p0 = 0; p0 < pn; p0 += 8) {
+            int st[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) st[k] = pstart[4 * min(p0 + k, pn - 1)];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) n_le += (p0 + k < pn && st[k] <= j[u]) ? 1 : 0;
+          }
+          if (n_le > 0) {
+            const i32x4 pt = ptab_s[pf + n_le - 1];   // start, count, first row
+            if (j[u] < pt.x + pt.y) row = pt.z + (j[u] - pt.x);
           }
         }
         dst[i] = row;
@@ -738,9 +775,9 @@ __global__ __launch_bounds__(64) void map_kernel(const int32_t* __restrict__ ids
 template <int M>
 hipError_t launch_map(const moonep_sizes& s, const int32_t* ids, const float* w, int32_t* plan,
                       const int32_t* ws, hipStream_t st) {
-  const size_t lds = (size_t)(5 * s.E + 4 * s.P_max) * sizeof(int32_t);
-  hipLaunchKernelGGL(map_kernel<M>, dim3(s.nblk * kMapWaves), dim3(64), lds, st, ids, w, plan,
-                     ws, s);
+  const size_t lds = (size_t)16 * (s.E + s.P_max) + 4 * ((s.E + 1) & ~1) + 8 * (s.E + 1);
+  hipLaunchKernelGGL(map_kernel<M>, dim3(s.nblk * kMapWaves * map_split(s)), dim3(64), lds, st,
+                     ids, w, plan, ws, s);
   return hipGetLastError();
 }
 
@@ -770,13 +807,11 @@ hipError_t launch_plan(const moonep_sizes& s, const int32_t* ids, const float* w
   hipLaunchKernelGGL(planner_kernel, dim3(1), dim3(kPlanThreads), plds, st, plan, ws, s);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  switch (s.blk / kMapThreads) {
+  switch (map_chunks(s)) {
     case 1: return launch_map<1>(s, ids, w, plan, ws, st);
     case 2: return launch_map<2>(s, ids, w, plan, ws, st);
     case 4: return launch_map<4>(s, ids, w, plan, ws, st);
     case 8: return launch_map<8>(s, ids, w, plan, ws, st);
-    case 16: return launch_map<16>(s, ids, w, plan, ws, st);
-    case 32: return launch_map<32>(s, ids, w, plan, ws, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -127,6 +127,20 @@ def test_random_cases(R, E, K, S, slots, H, mv):
     full_case(R, E, K, S, slots, H, ids.numpy(), wt.numpy(), seed, G_el=8 if slots else 0)
 
 
+@pytest.mark.parametrize("R,E,K,S,slots,H,mv", [
+    (4, 1024, 8, 8192, 4, 16, 1.0),    # 16 chunks per histogram wave: map parts of 8
+    (8, 1024, 8, 8100, 8, 8, 3.0),     # 32 chunks per wave, 4 parts, ragged last block
+])
+def test_split_map_waves(R, E, K, S, slots, H, mv):
+    """Large assignment counts with many experts: each histogram wave's range is mapped by
+    several waves, each starting from the counts the histogram recorded for it."""
+    sz = M.moonep_query(R, E, K, S, slots)
+    assert sz.blk // 512 > 8, "case must split histogram waves"
+    seed = 5150 + S
+    ids, wt, _, _ = make_routing(R, E, K, S, mv, seed, device="cuda")
+    full_case(R, E, K, S, slots, H, ids.cpu().numpy(), wt.cpu().numpy(), seed)
+
+
 def _cut_prefix(p):
     """For coverage only: how many shedding experts (in plan order) come before the first
     one that, were there no slot budget, would give some rank more than `slots` pieces.
