@@ -51,6 +51,25 @@ def reduce_bytes(plan_pieces, G_el):
     return sum((n + 2) * 4 * G_el for n in per.values())
 
 
+def pctl(vals, q):
+    """q-th percentile of a list (linear interpolation between order statistics)."""
+    v = sorted(vals)
+    x = (len(v) - 1) * q / 100.0
+    lo = int(x)
+    hi = min(lo + 1, len(v) - 1)
+    return v[lo] + (v[hi] - v[lo]) * (x - lo)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def measured_traffic(kernel_prefix, workload):
     """HBM bytes per launch of one kernel, from the committed rocprofv3 counter record
     (FETCH_SIZE and WRITE_SIZE, each scaled by a 4 GiB copy's reading).  None when there
@@ -119,6 +138,7 @@ def cpu_baseline(wl, ids_np, w_np, x_np, budget_s=15.0):
                   f"{wl.T} tokens ({td:.2f} s + {tc:.2f} s, median of {reps}); numpy, 1 thread",
         "plan_ms": round(t_plan * 1e3, 2),
         "host_cpus": len(os.sched_getaffinity(0)),
+        "host_cpu_model": cpu_model(),
     }
 
 
@@ -234,6 +254,9 @@ def main():
         row = dict(maxvio=b["maxvio"], achieved_maxvio=round(b["achieved"], 3),
                    plan_us=round(statistics.median(d["plan"]), 2),
                    dispatch_us=round(td, 2), combine_us=round(tc, 2),
+                   p10_p90_us={k: [round(pctl(d[v], 10), 2), round(pctl(d[v], 90), 2)]
+                               for k, v in (("plan", "plan"), ("dispatch", "disp"),
+                                            ("combine", "comb"))},
                    dispatch_gbps=round(db / td / 1e3, 1), combine_gbps=round(cb / tc / 1e3, 1),
                    dc_gbps=round((db + cb) / (td + tc) / 1e3, 1),
                    n_replicas=st["n_replicas"], n_fallback=st["n_fallback"],
