@@ -117,6 +117,10 @@ CASES = [
     (5, 10, 10, 33, 2, 8, 0.0001),     # K = E: every token takes every expert
     (8, 32, 7, 2049, 4, 16, 2.5),      # several map blocks with a ragged last block
     (32, 1024, 32, 64, 8, 8, 3.0),     # the largest E and K
+    (8, 8, 2, 50, 2, 16, 2.0),         # one expert per rank
+    (4, 16, 3, 1, 4, 8, 1.0),          # one token per rank
+    (4, 8, 2, 300, 256, 8, 3.0),       # the largest slot budget
+    (64, 64, 4, 16, 1, 8, 5.0),        # 64 ranks, one expert and one slot each
 ]
 
 
