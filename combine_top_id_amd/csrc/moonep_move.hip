@@ -45,33 +45,61 @@ void row_shape(int nvec, int umax, int upref, int* threads, int* u) {
 // ---------------------------------------------------------------------------------------
 // dispatch: recv[dst_row[t, k]] = x[t]
 // ---------------------------------------------------------------------------------------
-// One workgroup per token: each thread loads U vectors of the row, then stores them to
-// each of the token's K destination rows.  Plain (cached) loads and stores: measured on
-// MI355X, non-temporal stores to the scattered destination rows were about 5% slower.
-template <int U>
+// One workgroup per token: each thread loads U vectors of the row, then stores each of
+// them to the token's K destination rows in turn.  Plain (cached) loads and stores:
+// measured on MI355X, non-temporal stores to the scattered destination rows were about
+// 5% slower, non-temporal loads of x 2% slower, and storing one vector to all K rows
+// before the next vector about 1.5% faster than writing the rows one after another.
+// KT = K when K is a compile-time constant (the rows are then held in registers), else 0.
+template <int KT, int U>
 __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t* __restrict__ dst,
                                                        const u32x4* __restrict__ x,
-                                                       u32x4* __restrict__ recv, int K,
+                                                       u32x4* __restrict__ recv, int Krt,
                                                        int nvec, int nrows) {
+  const int K = KT > 0 ? KT : Krt;
   const int64_t t = blockIdx.x;
   const int32_t* d = dst ? dst + t * K : nullptr;   // null: staging row t*K + k
   const u32x4* src = x + t * nvec;
   const int step = blockDim.x * U;
-  for (int v0 = threadIdx.x; v0 < nvec; v0 += step) {
-    u32x4 buf[U];
+  if constexpr (KT > 0) {
+    int rows[KT];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int v = v0 + u * blockDim.x;
-      if (v < nvec) buf[u] = src[v];
-    }
-    for (int k = 0; k < K; ++k) {
-      const int row = d ? d[k] : (int)(t * K + k);
-      if ((unsigned)row >= (unsigned)nrows) continue;   // -1: unmapped
-      u32x4* o = recv + (int64_t)row * nvec;
+    for (int k = 0; k < KT; ++k) rows[k] = d ? d[k] : (int)(t * K + k);
+    for (int v0 = threadIdx.x; v0 < nvec; v0 += step) {
+      u32x4 buf[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int v = v0 + u * blockDim.x;
-        if (v < nvec) o[v] = buf[u];
+        if (v < nvec) buf[u] = src[v];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + u * blockDim.x;
+        if (v < nvec) {
+#pragma unroll
+          for (int k = 0; k < KT; ++k)
+            if ((unsigned)rows[k] < (unsigned)nrows)      // -1: unmapped
+              recv[(int64_t)rows[k] * nvec + v] = buf[u];
+        }
+      }
+    }
+  } else {
+    for (int v0 = threadIdx.x; v0 < nvec; v0 += step) {
+      u32x4 buf[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + u * blockDim.x;
+        if (v < nvec) buf[u] = src[v];
+      }
+      for (int k = 0; k < K; ++k) {
+        const int row = d ? d[k] : (int)(t * K + k);
+        if ((unsigned)row >= (unsigned)nrows) continue;   // -1: unmapped
+        u32x4* o = recv + (int64_t)row * nvec;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int v = v0 + u * blockDim.x;
+          if (v < nvec) o[v] = buf[u];
+        }
       }
     }
   }
@@ -446,12 +474,23 @@ __global__ __launch_bounds__(kRedThreads) void reduce_kernel(const int32_t* __re
 }
 
 
-template <int U>
-void launch_dispatch_u(const moonep_sizes& s, const int32_t* dst, int nrows, const uint16_t* x,
-                       uint16_t* recv, int nvec, int threads, hipStream_t st) {
-  hipLaunchKernelGGL(dispatch_kernel<U>, dim3((unsigned)s.T), dim3(threads), 0, st, dst,
+template <int KT, int U>
+void launch_dispatch_ku(const moonep_sizes& s, const int32_t* dst, int nrows, const uint16_t* x,
+                        uint16_t* recv, int nvec, int threads, hipStream_t st) {
+  hipLaunchKernelGGL((dispatch_kernel<KT, U>), dim3((unsigned)s.T), dim3(threads), 0, st, dst,
                      reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(recv), s.K,
                      nvec, nrows);
+}
+
+template <int KT>
+void launch_dispatch_k(const moonep_sizes& s, const int32_t* dst, int nrows, const uint16_t* x,
+                       uint16_t* recv, int nvec, int threads, int u, hipStream_t st) {
+  switch (u) {
+    case 1: launch_dispatch_ku<KT, 1>(s, dst, nrows, x, recv, nvec, threads, st); break;
+    case 2: launch_dispatch_ku<KT, 2>(s, dst, nrows, x, recv, nvec, threads, st); break;
+    case 3: launch_dispatch_ku<KT, 3>(s, dst, nrows, x, recv, nvec, threads, st); break;
+    default: launch_dispatch_ku<KT, 4>(s, dst, nrows, x, recv, nvec, threads, st); break;
+  }
 }
 
 template <int KT, int U, bool WEIGHTED>
@@ -481,16 +520,14 @@ hipError_t dispatch_rows(const moonep_sizes& s, const int32_t* dst, int nrows, c
                          int H, uint16_t* recv, hipStream_t st) {
   const int nvec = H / 8;
   int threads = 64, u = 1;
-  row_shape(nvec, 8, 7, &threads, &u);
-  switch (u) {
-    case 1: launch_dispatch_u<1>(s, dst, nrows, x, recv, nvec, threads, st); break;
-    case 2: launch_dispatch_u<2>(s, dst, nrows, x, recv, nvec, threads, st); break;
-    case 3: launch_dispatch_u<3>(s, dst, nrows, x, recv, nvec, threads, st); break;
-    case 4: launch_dispatch_u<4>(s, dst, nrows, x, recv, nvec, threads, st); break;
-    case 5: launch_dispatch_u<5>(s, dst, nrows, x, recv, nvec, threads, st); break;
-    case 6: launch_dispatch_u<6>(s, dst, nrows, x, recv, nvec, threads, st); break;
-    case 7: launch_dispatch_u<7>(s, dst, nrows, x, recv, nvec, threads, st); break;
-    default: launch_dispatch_u<8>(s, dst, nrows, x, recv, nvec, threads, st); break;
+  row_shape(nvec, 4, 2, &threads, &u);
+  switch (s.K) {
+    case 1: launch_dispatch_k<1>(s, dst, nrows, x, recv, nvec, threads, u, st); break;
+    case 2: launch_dispatch_k<2>(s, dst, nrows, x, recv, nvec, threads, u, st); break;
+    case 4: launch_dispatch_k<4>(s, dst, nrows, x, recv, nvec, threads, u, st); break;
+    case 6: launch_dispatch_k<6>(s, dst, nrows, x, recv, nvec, threads, u, st); break;
+    case 8: launch_dispatch_k<8>(s, dst, nrows, x, recv, nvec, threads, u, st); break;
+    default: launch_dispatch_k<0>(s, dst, nrows, x, recv, nvec, threads, u, st); break;
   }
   return hipGetLastError();
 }
