@@ -15,6 +15,8 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+constexpr int64_t kLastLevelCacheBytes = 256ll << 20;   // MI355X Infinity Cache
+
 __device__ __forceinline__ float bf_lo(unsigned int v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf_hi(unsigned int v) { return __uint_as_float(v & 0xFFFF0000u); }
 
@@ -46,12 +48,15 @@ void row_shape(int nvec, int umax, int upref, int* threads, int* u) {
 // dispatch: recv[dst_row[t, k]] = x[t]
 // ---------------------------------------------------------------------------------------
 // One workgroup per token: each thread loads U vectors of the row, then stores each of
-// them to the token's K destination rows in turn.  Plain (cached) loads and stores:
-// measured on MI355X, non-temporal stores to the scattered destination rows were about
-// 5% slower, non-temporal loads of x 2% slower, and storing one vector to all K rows
-// before the next vector about 1.5% faster than writing the rows one after another.
+// them to the token's K destination rows in turn.  Measured on MI355X: storing one
+// vector to all K rows before the next is about 1.5% faster than writing the rows one
+// after another, and non-temporal loads of x are 2% slower.  Stores: when the whole
+// destination buffer fits the 256 MB last-level cache, plain stores leave it dirty there
+// and the next kernel pays for the write-back (a combine reading it right after took 45%
+// longer), so the stores are non-temporal (NTS); for larger buffers non-temporal stores
+// are 5-8% slower and plain stores are used.
 // KT = K when K is a compile-time constant (the rows are then held in registers), else 0.
-template <int KT, int U>
+template <int KT, int U, bool NTS>
 __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t* __restrict__ dst,
                                                        const u32x4* __restrict__ x,
                                                        u32x4* __restrict__ recv, int Krt,
@@ -78,8 +83,10 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t* __restric
         if (v < nvec) {
 #pragma unroll
           for (int k = 0; k < KT; ++k)
-            if ((unsigned)rows[k] < (unsigned)nrows)      // -1: unmapped
-              recv[(int64_t)rows[k] * nvec + v] = buf[u];
+            if ((unsigned)rows[k] < (unsigned)nrows) {    // -1: unmapped
+              u32x4* o = recv + (int64_t)rows[k] * nvec + v;
+              if constexpr (NTS) __builtin_nontemporal_store(buf[u], o); else *o = buf[u];
+            }
         }
       }
     }
@@ -98,7 +105,9 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t* __restric
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int v = v0 + u * blockDim.x;
-          if (v < nvec) o[v] = buf[u];
+          if (v < nvec) {
+            if constexpr (NTS) __builtin_nontemporal_store(buf[u], o + v); else o[v] = buf[u];
+          }
         }
       }
     }
@@ -477,9 +486,15 @@ __global__ __launch_bounds__(kRedThreads) void reduce_kernel(const int32_t* __re
 template <int KT, int U>
 void launch_dispatch_ku(const moonep_sizes& s, const int32_t* dst, int nrows, const uint16_t* x,
                         uint16_t* recv, int nvec, int threads, hipStream_t st) {
-  hipLaunchKernelGGL((dispatch_kernel<KT, U>), dim3((unsigned)s.T), dim3(threads), 0, st, dst,
-                     reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(recv), s.K,
-                     nvec, nrows);
+  const bool fits_llc = (int64_t)nrows * nvec * 16 <= kLastLevelCacheBytes;
+  if (fits_llc)
+    hipLaunchKernelGGL((dispatch_kernel<KT, U, true>), dim3((unsigned)s.T), dim3(threads), 0, st,
+                       dst, reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(recv), s.K,
+                       nvec, nrows);
+  else
+    hipLaunchKernelGGL((dispatch_kernel<KT, U, false>), dim3((unsigned)s.T), dim3(threads), 0, st,
+                       dst, reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(recv), s.K,
+                       nvec, nrows);
 }
 
 template <int KT>
