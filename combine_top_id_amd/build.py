@@ -28,6 +28,25 @@ def build(verbose=False):
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + r.stderr[-4000:])
     os.replace(tmp, out)
+    build_c_smoke(verbose)
+    return out
+
+
+def build_c_smoke(verbose=False):
+    """A plain C consumer of the C ABI (tests/c_abi/smoke.c), linked against the library
+    just built; the library is found next to it through a relative run path."""
+    src = os.path.join(ROOT, "tests", "c_abi", "smoke.c")
+    out = os.path.join(ROOT, "tests", "c_abi", "smoke")
+    cmd = ["gcc", "-std=c11", "-O1", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+           "-I", "/opt/rocm/include", src, "-L", HERE, "-lmoonep", "-L", "/opt/rocm/lib",
+           "-lamdhip64", "-Wl,-rpath,$ORIGIN/../../combine_top_id_amd",
+           "-Wl,-rpath,/opt/rocm/lib", "-o", out + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("gcc failed:\n" + r.stderr[-4000:])
+    os.replace(out + ".tmp", out)
     return out
 
 
