@@ -139,7 +139,6 @@ __device__ __forceinline__ bool before(int la, int a, int lb, int b) {
   return la > lb || (la == lb && a < b);
 }
 
-constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kColRegs = 32;   // block counts a column thread keeps in registers
 
 __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restrict__ plan,
