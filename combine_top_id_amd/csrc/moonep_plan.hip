@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
                                     // pieces exist
   __shared__ int32_t hl_s[64], used_s[64], fb_s[64], nfb_s[64], sr_s[64], ht_s[64], dend_s[64],
       xs_s[64], wtot_s[kPlanThreads / 64];
-  __shared__ int bad_s, nshed_s, npieces_s, maxload_s, err_s;
+  __shared__ int bad_s, nshed_s, npieces_s, err_s;
 
   int32_t* hdr = plan + s.o_hdr;
   const int tid = threadIdx.x;
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
   // ws[b][e] holds block b's count of expert e.  Each column is split into `tpc` segments
   // of consecutive blocks, one thread per (segment, expert): segment sums, then the
   // exclusive scan over blocks, kept in registers and written back at the very end.
-  if (tid == 0) { bad_s = INT_MAX; maxload_s = 0; err_s = 0; }
+  if (tid == 0) { bad_s = INT_MAX; err_s = 0; }
   const int nblk = s.nblk;
   int tpc = 1;
   while (tpc * 2 * E <= kPlanThreads && tpc * 2 <= nblk) tpc *= 2;
@@ -212,16 +212,10 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
   __syncthreads();
   if (mybad != INT_MAX) atomicMin(&bad_s, mybad);
   int colbase = 0;   // the column thread's first base (blocks before b0)
-  int mytotal = 0;
   if (col_thread) {
     for (int g = 0; g < cg; ++g) colbase += part_s[g * E + ce];
-    if (cg == tpc - 1) {
-      mytotal = colbase + part_s[cg * E + ce];
-      load_s[ce] = mytotal;
-    }
+    if (cg == tpc - 1) load_s[ce] = colbase + part_s[cg * E + ce];
   }
-  for (int off = 32; off >= 1; off >>= 1) mytotal = max(mytotal, __shfl_xor(mytotal, off, 64));
-  if (lane == 0 && mytotal > 0) atomicMax(&maxload_s, mytotal);
   __syncthreads();
   if (tid < R) {
     // home load of rank tid (independent LDS reads, unrolled)
@@ -279,6 +273,33 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
     pnum_s[e] = 0;
   }
   __syncthreads();
+
+  // per-block bases for the map kernel, written over the counts
+  auto write_bases = [&]() {
+    int run = colbase;
+    if (in_regs) {
+#pragma unroll
+      for (int u = 0; u < kColRegs; ++u) {
+        if (b0 + u < b1) {
+          ws[(int64_t)(b0 + u) * E + ce] = run;
+          run += v[u];
+        }
+      }
+    } else {
+      for (int b = b0; b < b1; b += kColRegs) {
+        int w[kColRegs];
+#pragma unroll
+        for (int u = 0; u < kColRegs; ++u) w[u] = b + u < b1 ? ws[(int64_t)(b + u) * E + ce] : 0;
+#pragma unroll
+        for (int u = 0; u < kColRegs; ++u) {
+          if (b + u < b1) {
+            ws[(int64_t)(b + u) * E + ce] = run;
+            run += w[u];
+          }
+        }
+      }
+    }
+  };
 
   // ---- wave 0: order the shedding experts, then place them --------------------------------
   if (wave == 0) {
@@ -461,6 +482,8 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
     sr_s[lane] = slotrows;
     if (__ballot(err || (lane < R && D != 0))) { if (lane == 0) err_s = 1; }
     if (lane == 0) { npieces_s = min(np, PM); nshed_s = nshed; }
+  } else if (col_thread) {
+    write_bases();     // the other waves are idle until the layout: write their bases now
   }
   __syncthreads();
 
@@ -532,32 +555,7 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
     reinterpret_cast<i32x4*>(plan + s.o_xtab)[e] =
         i32x4{keep_s[e], home_s[e], pfirst_s[e], pnum_s[e]};
   }
-  if (col_thread) {
-    // per-block bases for the map kernel
-    int run = colbase;
-    if (in_regs) {
-#pragma unroll
-      for (int u = 0; u < kColRegs; ++u) {
-        if (b0 + u < b1) {
-          ws[(int64_t)(b0 + u) * E + ce] = run;
-          run += v[u];
-        }
-      }
-    } else {
-      for (int b = b0; b < b1; b += kColRegs) {
-        int w[kColRegs];
-#pragma unroll
-        for (int u = 0; u < kColRegs; ++u) w[u] = b + u < b1 ? ws[(int64_t)(b + u) * E + ce] : 0;
-#pragma unroll
-        for (int u = 0; u < kColRegs; ++u) {
-          if (b + u < b1) {
-            ws[(int64_t)(b + u) * E + ce] = run;
-            run += w[u];
-          }
-        }
-      }
-    }
-  }
+  if (col_thread && wave == 0) write_bases();
   if (wave == 0) {
     // experts with slot replicas, in plan order (the reduce work list)
     const int nshed = nshed_s;
@@ -576,10 +574,13 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
     }
     // statistics over ranks (lane r)
     int nrep = used_s[lane], nfb = nfb_s[lane], ppr = used_s[lane] + nfb_s[lane];
+    int maxload = 0;
+    for (int e = lane; e < E; e += 64) maxload = max(maxload, load_s[e]);
     for (int d = 32; d >= 1; d >>= 1) {
       nrep += __shfl_xor(nrep, d, 64);
       nfb += __shfl_xor(nfb, d, 64);
       ppr = max(ppr, __shfl_xor(ppr, d, 64));
+      maxload = max(maxload, __shfl_xor(maxload, d, 64));
     }
     const bool err = err_s != 0;
     int val = 0;
@@ -593,7 +594,7 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
       case H_NRED: val = err ? 0 : n; break;
       case H_BADIDX: val = -1; break;
       case H_NSHED: val = nshed; break;
-      case H_MAXLOAD: val = maxload_s; break;
+      case H_MAXLOAD: val = maxload; break;
       case H_R: val = R; break;
       case H_E: val = E; break;
       case H_K: val = s.K; break;
