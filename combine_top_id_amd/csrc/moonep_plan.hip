@@ -416,6 +416,9 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
      const int q_e = qq < nshed ? order_s[qq] : 0;
      const int q_shed = qq < nshed ? shed_s[q_e] : 0;
      const int q_keep = qq < nshed ? keep_s[q_e] : 0;
+     // wait for these loads here: otherwise the loop below waits on every iteration, unable
+     // to tell them from its own outstanding LDS stores (lgkmcnt(0); vmcnt, expcnt untouched)
+     __builtin_amdgcn_s_waitcnt(0xC07F);
      const int qn = min(64, nshed - q0);
      for (int qi = 0; qi < qn; ++qi) {
       const int e = __builtin_amdgcn_readlane(q_e, qi);
