@@ -95,9 +95,11 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _dev(t, dtype, name):
+def _dev(t, dtype, name, device=None):
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise MoonepError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise MoonepError(f"{name} is on {t.device}, the plan on {device}")
     if t.dtype != dtype:
         raise MoonepError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
@@ -167,6 +169,7 @@ def moonep_plan(topk_ids, topk_w, R, E, K, S, slots, plan=None, stream=None) -> 
 
 def moonep_dispatch(plan: Plan, x, recv=None, stream=None):
     """recv[dst_row[t, k]] = x[t]; x is bf16 [T, H]; returns recv bf16 [R*NvS, H]."""
+    D = plan.blob.device
     H = x.shape[-1]
     if x.numel() != plan.sz.T * H:
         raise MoonepError("x must be [T, H]")
@@ -174,13 +177,14 @@ def moonep_dispatch(plan: Plan, x, recv=None, stream=None):
         recv = torch.empty(plan.sz.recv_rows, H, dtype=torch.bfloat16, device=x.device)
     if recv.numel() != plan.sz.recv_rows * H:
         raise MoonepError("recv must be [R*NvS, H]")
-    _check(lib().moonep_dispatch(ctypes.byref(plan.desc), _dev(x, torch.bfloat16, "x"), H,
-                                 _dev(recv, torch.bfloat16, "recv"), _stream(stream)))
+    _check(lib().moonep_dispatch(ctypes.byref(plan.desc), _dev(x, torch.bfloat16, "x", D), H,
+                                 _dev(recv, torch.bfloat16, "recv", D), _stream(stream)))
     return recv
 
 
 def moonep_combine(plan: Plan, y, out=None, stream=None):
     """out[t] = bf16(sum_k w[t,k] * y[dst_row[t,k]]); y bf16 [R*NvS, H] -> out bf16 [T, H]."""
+    D = plan.blob.device
     H = y.shape[-1]
     if y.numel() != plan.sz.recv_rows * H:
         raise MoonepError("y must be [R*NvS, H]")
@@ -188,8 +192,8 @@ def moonep_combine(plan: Plan, y, out=None, stream=None):
         out = torch.empty(plan.sz.T, H, dtype=torch.bfloat16, device=y.device)
     if out.numel() != plan.sz.T * H:
         raise MoonepError("out must be [T, H]")
-    _check(lib().moonep_combine(ctypes.byref(plan.desc), _dev(y, torch.bfloat16, "y"), H,
-                                _dev(out, torch.bfloat16, "out"), _stream(stream)))
+    _check(lib().moonep_combine(ctypes.byref(plan.desc), _dev(y, torch.bfloat16, "y", D), H,
+                                _dev(out, torch.bfloat16, "out", D), _stream(stream)))
     return out
 
 
@@ -203,30 +207,33 @@ def _stage(plan, H, stage, device):
 
 def moonep_dispatch_staged(plan: Plan, x, recv=None, stage=None, stream=None):
     """Non-zero-copy dispatch: x -> stage (arrival order) -> recv (epilogue copy)."""
+    D = plan.blob.device
     H = x.shape[-1]
     stage = _stage(plan, H, stage, x.device)
     if recv is None:
         recv = torch.empty(plan.sz.recv_rows, H, dtype=torch.bfloat16, device=x.device)
-    _check(lib().moonep_dispatch_staged(ctypes.byref(plan.desc), _dev(x, torch.bfloat16, "x"), H,
-                                        _dev(stage, torch.bfloat16, "stage"),
-                                        _dev(recv, torch.bfloat16, "recv"), _stream(stream)))
+    _check(lib().moonep_dispatch_staged(ctypes.byref(plan.desc), _dev(x, torch.bfloat16, "x", D), H,
+                                        _dev(stage, torch.bfloat16, "stage", D),
+                                        _dev(recv, torch.bfloat16, "recv", D), _stream(stream)))
     return recv
 
 
 def moonep_combine_staged(plan: Plan, y, out=None, stage=None, stream=None):
     """Non-zero-copy combine: y -> stage (prologue copy) -> weighted sum -> out."""
+    D = plan.blob.device
     H = y.shape[-1]
     stage = _stage(plan, H, stage, y.device)
     if out is None:
         out = torch.empty(plan.sz.T, H, dtype=torch.bfloat16, device=y.device)
-    _check(lib().moonep_combine_staged(ctypes.byref(plan.desc), _dev(y, torch.bfloat16, "y"), H,
-                                       _dev(stage, torch.bfloat16, "stage"),
-                                       _dev(out, torch.bfloat16, "out"), _stream(stream)))
+    _check(lib().moonep_combine_staged(ctypes.byref(plan.desc), _dev(y, torch.bfloat16, "y", D), H,
+                                       _dev(stage, torch.bfloat16, "stage", D),
+                                       _dev(out, torch.bfloat16, "out", D), _stream(stream)))
     return out
 
 
 def moonep_dispatch_bwd(plan: Plan, g_recv, gx=None, stream=None):
     """gx[t] = bf16(sum_k g_recv[dst_row[t,k]]); g_recv bf16 [R*NvS, H] -> gx bf16 [T, H]."""
+    D = plan.blob.device
     H = g_recv.shape[-1]
     if g_recv.numel() != plan.sz.recv_rows * H:
         raise MoonepError("g_recv must be [R*NvS, H]")
@@ -234,14 +241,16 @@ def moonep_dispatch_bwd(plan: Plan, g_recv, gx=None, stream=None):
         gx = torch.empty(plan.sz.T, H, dtype=torch.bfloat16, device=g_recv.device)
     if gx.numel() != plan.sz.T * H:
         raise MoonepError("gx must be [T, H]")
-    _check(lib().moonep_dispatch_bwd(ctypes.byref(plan.desc), _dev(g_recv, torch.bfloat16, "g_recv"),
-                                     H, _dev(gx, torch.bfloat16, "gx"), _stream(stream)))
+    _check(lib().moonep_dispatch_bwd(ctypes.byref(plan.desc),
+                                     _dev(g_recv, torch.bfloat16, "g_recv", D),
+                                     H, _dev(gx, torch.bfloat16, "gx", D), _stream(stream)))
     return gx
 
 
 def moonep_combine_bwd(plan: Plan, dout, y, g_y=None, dw=None, stream=None):
     """g_y[dst_row[t,k]] = bf16(w[t,k] * dout[t]); dw[t,k] = <dout[t], y[dst_row[t,k]]>.
     dout bf16 [T, H], y bf16 [R*NvS, H]; returns (g_y bf16 [R*NvS, H], dw fp32 [T, K])."""
+    D = plan.blob.device
     H = dout.shape[-1]
     if dout.numel() != plan.sz.T * H or y.numel() != plan.sz.recv_rows * H:
         raise MoonepError("dout must be [T, H] and y [R*NvS, H]")
@@ -251,16 +260,17 @@ def moonep_combine_bwd(plan: Plan, dout, y, g_y=None, dw=None, stream=None):
         dw = torch.empty(plan.sz.T, plan.sz.K, dtype=torch.float32, device=dout.device)
     if g_y.numel() != plan.sz.recv_rows * H or dw.numel() != plan.sz.T * plan.sz.K:
         raise MoonepError("g_y must be [R*NvS, H] and dw [T, K]")
-    _check(lib().moonep_combine_bwd(ctypes.byref(plan.desc), _dev(dout, torch.bfloat16, "dout"),
-                                    _dev(y, torch.bfloat16, "y"), H,
-                                    _dev(g_y, torch.bfloat16, "g_y"),
-                                    _dev(dw, torch.float32, "dw"), _stream(stream)))
+    _check(lib().moonep_combine_bwd(ctypes.byref(plan.desc), _dev(dout, torch.bfloat16, "dout", D),
+                                    _dev(y, torch.bfloat16, "y", D), H,
+                                    _dev(g_y, torch.bfloat16, "g_y", D),
+                                    _dev(dw, torch.float32, "dw", D), _stream(stream)))
     return g_y, dw
 
 
 def moonep_prefetch_weight(plan: Plan, home_w, slot_w=None, stream=None):
     """slot_w[r, slot] = home_w[e] for every slot piece; home_w bf16 [E, W_el] ->
     slot_w bf16 [R, slots, W_el]."""
+    D = plan.blob.device
     W_el = home_w.shape[-1]
     if home_w.numel() != plan.sz.E * W_el:
         raise MoonepError("home_w must be [E, W_el]")
@@ -269,38 +279,49 @@ def moonep_prefetch_weight(plan: Plan, home_w, slot_w=None, stream=None):
                              device=home_w.device)
     if slot_w.numel() != plan.sz.R * plan.sz.slots * W_el:
         raise MoonepError("slot_w must be [R, slots, W_el]")
-    sp = _dev(slot_w, torch.bfloat16, "slot_w") if slot_w.numel() else ctypes.c_void_p(0)
+    sp = _dev(slot_w, torch.bfloat16, "slot_w", D) if slot_w.numel() else ctypes.c_void_p(0)
     _check(lib().moonep_prefetch_weight(ctypes.byref(plan.desc),
-                                        _dev(home_w, torch.bfloat16, "home_w"), W_el, sp,
+                                        _dev(home_w, torch.bfloat16, "home_w", D), W_el, sp,
                                         _stream(stream)))
     return slot_w
 
 
 def moonep_expert_stub(plan: Plan, topk_ids, recv, home_w, slot_w, y=None, stream=None):
     """y[row] = bf16(recv[row] * W[:H]) with W the weight slab the row's group reads."""
+    D = plan.blob.device
     H = recv.shape[-1]
     W_el = home_w.shape[-1]
+    if topk_ids.numel() != plan.sz.A:
+        raise MoonepError("topk_ids must hold R*S*K elements")
+    if recv.numel() != plan.sz.recv_rows * H:
+        raise MoonepError("recv must be [R*NvS, H]")
+    if home_w.numel() != plan.sz.E * W_el or slot_w.numel() != plan.sz.R * plan.sz.slots * W_el:
+        raise MoonepError("home_w must be [E, W_el] and slot_w [R, slots, W_el]")
     if y is None:
         y = torch.empty_like(recv)
-    sp = _dev(slot_w, torch.bfloat16, "slot_w") if slot_w.numel() else ctypes.c_void_p(0)
-    _check(lib().moonep_expert_stub(ctypes.byref(plan.desc), _dev(topk_ids, torch.int32, "topk_ids"),
-                                    _dev(recv, torch.bfloat16, "recv"),
-                                    _dev(home_w, torch.bfloat16, "home_w"), sp, W_el, H,
-                                    _dev(y, torch.bfloat16, "y"), _stream(stream)))
+    if y.numel() != recv.numel():
+        raise MoonepError("y must be [R*NvS, H]")
+    sp = _dev(slot_w, torch.bfloat16, "slot_w", D) if slot_w.numel() else ctypes.c_void_p(0)
+    _check(lib().moonep_expert_stub(ctypes.byref(plan.desc),
+                                    _dev(topk_ids, torch.int32, "topk_ids", D),
+                                    _dev(recv, torch.bfloat16, "recv", D),
+                                    _dev(home_w, torch.bfloat16, "home_w", D), sp, W_el, H,
+                                    _dev(y, torch.bfloat16, "y", D), _stream(stream)))
     return y
 
 
 def moonep_reduce_grad(plan: Plan, home_grad, rep_grad, stream=None):
     """home_grad[e] += replica slabs of e (in place); home fp32 [E, G_el], rep fp32
     [R, slots, G_el]."""
+    D = plan.blob.device
     G_el = home_grad.shape[-1]
     if home_grad.numel() != plan.sz.E * G_el:
         raise MoonepError("home_grad must be [E, G_el]")
     if rep_grad.numel() != plan.sz.R * plan.sz.slots * G_el:
         raise MoonepError("rep_grad must be [R, slots, G_el]")
-    rep_p = _dev(rep_grad, torch.float32, "rep_grad") if rep_grad.numel() else ctypes.c_void_p(0)
+    rep_p = _dev(rep_grad, torch.float32, "rep_grad", D) if rep_grad.numel() else ctypes.c_void_p(0)
     _check(lib().moonep_reduce_grad(ctypes.byref(plan.desc),
-                                    _dev(home_grad, torch.float32, "home_grad"), rep_p, G_el,
+                                    _dev(home_grad, torch.float32, "home_grad", D), rep_p, G_el,
                                     _stream(stream)))
     return home_grad
 
