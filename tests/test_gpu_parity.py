@@ -20,6 +20,7 @@ from gen import (TINY, SMALL, DSV3, KIMI, DECODE, make_routing, make_balanced_ro
 from oracle import moonep_oracle as O
 from tests.gpu_util import say, read_plan, assert_plan_matches, to_dev_ids
 from tests.tol import assert_close, RTOL_BF16, RTOL_FP32
+from tests import adversarial
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -143,6 +144,14 @@ def test_split_map_waves(R, E, K, S, slots, H, mv):
     seed = 5150 + S
     ids, wt, _, _ = make_routing(R, E, K, S, mv, seed, device="cuda")
     full_case(R, E, K, S, slots, H, ids.cpu().numpy(), wt.cpu().numpy(), seed)
+
+
+@pytest.mark.parametrize("case", adversarial.routings(), ids=lambda c: c[0])
+def test_adversarial_routings_on_gpu(case):
+    name, R, E, K, S, slots, ids = case
+    T = R * S
+    w = np.full((T, K), 1.0 / K, dtype=np.float32)
+    full_case(R, E, K, S, slots, 64, ids, w, 4100 + R + E + K, G_el=8 if slots else 0)
 
 
 def _cut_prefix(p):

@@ -30,6 +30,7 @@ import torch
 from gen import TINY, SMALL, make_routing, make_balanced_routing, make_hidden, make_scales, bf16_bits
 from oracle import moonep_oracle as O
 from tests.tol import assert_close, RTOL_FP32
+from tests import adversarial
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -250,6 +251,21 @@ def test_unit_step_and_merge_agree(seed):
         assert p.n_fallback == 0
         assert [tuple(x) for x in p.pieces.tolist()] == pieces_m
     assert (O.slot_map(p, ids) == streaming_slot_map(p, ids)).all()
+
+
+@pytest.mark.parametrize("case", adversarial.routings(), ids=lambda c: c[0])
+def test_adversarial_routings(case):
+    """Extreme routings (one expert takes every token, a rank with no load, everything on
+    one rank, identical routing, no slots): invariants hold and the one-assignment-at-a-
+    time derivation agrees."""
+    name, R, E, K, S, slots, ids = case
+    p = O.plan(ids, R, E, K, S, slots)
+    check_invariants(p, ids)
+    shed_u, pieces_u = unit_step_plan(p.load.tolist(), R, E, K, S, slots)
+    assert p.shed.tolist() == shed_u
+    assert [tuple(x) for x in p.pieces.tolist()] == pieces_u
+    assert (O.slot_map(p, ids) == streaming_slot_map(p, ids)).all()
+    assert p.n_pieces > 0
 
 
 def test_exhaustive_r2_e4_k1_s3():
