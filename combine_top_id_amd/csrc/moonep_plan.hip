@@ -11,18 +11,22 @@
 // workgroup, whose wave w owns the contiguous sub-block of 64*M assignments starting at
 // b*blk + w*64*M.  Three launches on the caller's stream:
 //   1. hist_kernel     per block: one LDS histogram per wave -> the block's expert counts
-//                      and, per wave, the count of earlier waves of the block; the first
-//                      invalid id of the block.
+//                      and, per wave, the count of earlier waves of the block (and, for
+//                      waves of more than 8 chunks, the wave's running counts at each
+//                      8-chunk boundary); the first invalid id of the block.
 //   2. planner_kernel  one workgroup: per-block bases (exclusive scan of the counts over
 //                      blocks), expert loads, per-rank excess and deficit, shedding,
-//                      greedy placement (one wave, lane r = rank r), buffer layout
-//                      (one wave per rank), piece rows, statistics.  Everything stays in
-//                      LDS until one final write of the plan.
+//                      greedy placement (wave 0, lane r = rank r: a parallel cut of the
+//                      shed stream up to the first expert that would overfill a slot
+//                      budget, then one expert at a time), buffer layout (one block-wide
+//                      scan), piece rows, statistics.  Everything stays in LDS until one
+//                      final write of the plan.
 //   3. map_kernel      one single-wave workgroup per map sub-block (a histogram wave's
 //                      sub-block, or a part of at most 8 chunks of it, whose starting
 //                      counts the histogram wave recorded): the stable rank j of each
-//                      assignment among its expert's assignments (ballot peer masks and an
-//                      LDS counter per expert), then its row; copies the top-K weights.
+//                      assignment among its expert's assignments (per-id LDS peer masks
+//                      and an LDS counter per expert), then its row; copies the top-K
+//                      weights.
 #include <climits>
 
 #include "moonep_internal.h"
@@ -176,7 +180,8 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
   // ---- per-block bases and expert loads -----------------------------------------------------
   // ws[b][e] holds block b's count of expert e.  Each column is split into `tpc` segments
   // of consecutive blocks, one thread per (segment, expert): segment sums, then the
-  // exclusive scan over blocks, kept in registers and written back at the very end.
+  // exclusive scan over blocks, kept in registers and written back over the counts later
+  // (by the waves that are idle during placement; wave 0 at the end).
   if (tid == 0) { bad_s = INT_MAX; err_s = 0; }
   const int nblk = s.nblk;
   int tpc = 1;
