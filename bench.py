@@ -259,6 +259,8 @@ def main():
                                             ("combine", "comb"))},
                    dispatch_gbps=round(db / td / 1e3, 1), combine_gbps=round(cb / tc / 1e3, 1),
                    dc_gbps=round((db + cb) / (td + tc) / 1e3, 1),
+                   plan_plus_combine_us=round(statistics.median(
+                       [a + b for a, b in zip(d["plan"], d["comb"])]), 2),
                    n_replicas=st["n_replicas"], n_fallback=st["n_fallback"],
                    max_pieces_per_rank=st["max_pieces_per_rank"])
         if home is not None:
