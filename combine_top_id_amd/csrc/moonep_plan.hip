@@ -57,6 +57,18 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
+// Inclusive prefix maximum over the 64 lanes, same moves as wave_incl_scan; for values
+// >= 0 (lanes without a source read 0).
+__device__ __forceinline__ int wave_incl_max(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, kRowShr1, 0xf, 0xf, true));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, kRowShr2, 0xf, 0xf, true));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, kRowShr4, 0xf, 0xf, true));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, kRowShr8, 0xf, 0xf, true));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, kRowBcast15, 0xa, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, kRowBcast31, 0xc, 0xf, false));
+  return v;
+}
+
 __device__ __forceinline__ int lane63(int v) { return __builtin_amdgcn_readlane(v, 63); }
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
@@ -169,8 +181,8 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
   int32_t* part_s = pe_s;           // [kPlanThreads] column segment sums, used before the
                                     // pieces exist
   __shared__ int32_t hl_s[64], used_s[64], fb_s[64], nfb_s[64], sr_s[64], ht_s[64], dend_s[64],
-      xs_s[64], wtot_s[kPlanThreads / 64];
-  __shared__ int bad_s, nshed_s, npieces_s, err_s;
+      xs_s[64], wtot_s[kPlanThreads / 64], colbase0_s[64];
+  __shared__ int bad_s, nshed_s, npieces_s, err_s, maxload_s;
 
   int32_t* hdr = plan + s.o_hdr;
   const int tid = threadIdx.x;
@@ -221,6 +233,7 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
     for (int g = 0; g < cg; ++g) colbase += part_s[g * E + ce];
     if (cg == tpc - 1) load_s[ce] = colbase + part_s[cg * E + ce];
   }
+  if (wave == 0) colbase0_s[lane] = colbase;   // wave 1 writes wave 0's bases later
   __syncthreads();
   if (tid < R) {
     // home load of rank tid (independent LDS reads, unrolled)
@@ -490,8 +503,34 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
     sr_s[lane] = slotrows;
     if (__ballot(err || (lane < R && D != 0))) { if (lane == 0) err_s = 1; }
     if (lane == 0) { npieces_s = min(np, PM); nshed_s = nshed; }
-  } else if (col_thread) {
-    write_bases();     // the other waves are idle until the layout: write their bases now
+  } else {
+    // the other waves are idle until the layout: they write the block bases now, wave 1
+    // also wave 0's (its counts re-read, its first bases from colbase0_s), and wave 2
+    // finds the largest expert load for the statistics
+    if (col_thread) write_bases();
+    if (wave == 1 && lane < tpc * E) {
+      const int ce0 = lane % E, cg0 = lane / E;
+      const int bb1 = min(cg0 * seg + seg, nblk);
+      int run = colbase0_s[lane];
+      for (int b = cg0 * seg; b < bb1; b += kColRegs) {
+        int w[kColRegs];
+#pragma unroll
+        for (int u = 0; u < kColRegs; ++u) w[u] = b + u < bb1 ? ws[(int64_t)(b + u) * E + ce0] : 0;
+#pragma unroll
+        for (int u = 0; u < kColRegs; ++u) {
+          if (b + u < bb1) {
+            ws[(int64_t)(b + u) * E + ce0] = run;
+            run += w[u];
+          }
+        }
+      }
+    }
+    if (wave == 2) {
+      int m = 0;
+      for (int e = lane; e < E; e += 64) m = max(m, load_s[e]);
+      m = lane63(wave_incl_max(m));
+      if (lane == 0) maxload_s = m;
+    }
   }
   __syncthreads();
 
@@ -563,7 +602,6 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
     reinterpret_cast<i32x4*>(plan + s.o_xtab)[e] =
         i32x4{keep_s[e], home_s[e], pfirst_s[e], pnum_s[e]};
   }
-  if (col_thread && wave == 0) write_bases();
   if (wave == 0) {
     // experts with slot replicas, in plan order (the reduce work list)
     const int nshed = nshed_s;
@@ -581,15 +619,9 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
       n += __popcll(m);
     }
     // statistics over ranks (lane r)
-    int nrep = used_s[lane], nfb = nfb_s[lane], ppr = used_s[lane] + nfb_s[lane];
-    int maxload = 0;
-    for (int e = lane; e < E; e += 64) maxload = max(maxload, load_s[e]);
-    for (int d = 32; d >= 1; d >>= 1) {
-      nrep += __shfl_xor(nrep, d, 64);
-      nfb += __shfl_xor(nfb, d, 64);
-      ppr = max(ppr, __shfl_xor(ppr, d, 64));
-      maxload = max(maxload, __shfl_xor(maxload, d, 64));
-    }
+    const int nrep = lane63(wave_incl_scan(used_s[lane]));
+    const int nfb = lane63(wave_incl_scan(nfb_s[lane]));
+    const int ppr = lane63(wave_incl_max(used_s[lane] + nfb_s[lane]));
     const bool err = err_s != 0;
     int val = 0;
     switch (lane) {
@@ -602,7 +634,7 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
       case H_NRED: val = err ? 0 : n; break;
       case H_BADIDX: val = -1; break;
       case H_NSHED: val = nshed; break;
-      case H_MAXLOAD: val = maxload; break;
+      case H_MAXLOAD: val = maxload_s; break;
       case H_R: val = R; break;
       case H_E: val = E; break;
       case H_K: val = s.K; break;
