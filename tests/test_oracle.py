@@ -26,6 +26,7 @@ import os
 import numpy as np
 import pytest
 import torch
+from hypothesis import given, settings, strategies as st
 
 from gen import TINY, SMALL, make_routing, make_balanced_routing, make_hidden, make_scales, bf16_bits
 from oracle import moonep_oracle as O
@@ -306,6 +307,32 @@ def test_plan_depends_only_on_loads():
     perm = rng.permutation(ids.reshape(-1)).reshape(ids.shape)
     p2 = O.plan(perm, 4, 16, 2, 32, 4)
     assert (p1.pieces == p2.pieces).all() and (p1.off == p2.off).all()
+
+
+@st.composite
+def _load_problems(draw):
+    R = draw(st.integers(1, 6))
+    E = R * draw(st.integers(1, 4))
+    K = draw(st.integers(1, min(3, E)))
+    S = draw(st.integers(1, 6))
+    slots = draw(st.integers(0, 4))
+    A = R * S * K
+    cuts = sorted(draw(st.lists(st.integers(0, A), min_size=E - 1, max_size=E - 1)))
+    load = np.diff(np.array([0] + cuts + [A], dtype=np.int64))
+    return R, E, K, S, slots, load
+
+
+@settings(max_examples=400, deadline=None)
+@given(_load_problems())
+def test_plan_properties_on_searched_loads(prob):
+    """Property search over load vectors (any split of R*S*K assignments over E experts):
+    the plan keeps every invariant and equals the one-assignment-at-a-time derivation."""
+    R, E, K, S, slots, load = prob
+    p = O.plan_from_loads(load, O.sizes(R, E, K, S, slots))
+    check_invariants(p)
+    shed_u, pieces_u = unit_step_plan(load.tolist(), R, E, K, S, slots)
+    assert p.shed.tolist() == shed_u
+    assert [tuple(x) for x in p.pieces.tolist()] == pieces_u
 
 
 def test_loads_brute_force_and_bad_ids():
