@@ -156,6 +156,24 @@ def test_adversarial_routings_on_gpu(case):
     full_case(R, E, K, S, slots, 64, ids, w, 4100 + R + E + K, G_el=8 if slots else 0)
 
 
+@pytest.mark.parametrize("R,E,K,S,slots,mv", [
+    (64, 1024, 16, 1024, 8, 3.0),     # 64 blocks per column thread: two register rounds
+    (50, 1000, 16, 1010, 4, 8.0),     # 50 blocks: a ragged second round and last block
+])
+def test_long_block_columns(R, E, K, S, slots, mv):
+    """Many assignments with many experts: each planner thread scans more block counts than
+    it holds in registers, so the column scan and the bases it writes (wave 0's by wave 1)
+    take the multi-round path."""
+    sz = M.moonep_query(R, E, K, S, slots)
+    tpc = 1
+    while tpc * 2 * E <= 1024 and tpc * 2 <= sz.nblk:
+        tpc *= 2
+    assert (sz.nblk + tpc - 1) // tpc > 32, "case must exceed one register round"
+    seed = 6100 + R
+    ids, wt, _, _ = make_routing(R, E, K, S, mv, seed, device="cuda")
+    full_case(R, E, K, S, slots, 8, ids.cpu().numpy(), wt.cpu().numpy(), seed)
+
+
 def _cut_prefix(p):
     """For coverage only: how many shedding experts (in plan order) come before the first
     one that, were there no slot budget, would give some rank more than `slots` pieces.
