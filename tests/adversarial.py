@@ -35,4 +35,9 @@ def routings():
     T = R * S
     out.append(("the last expert of 1024 takes every token", R, E, K, S, 4,
                 _ids([[1023, t % 1023] for t in range(T)])))
+    R, E, K, S = 2, 1024, 4, 256
+    T = R * S
+    even = _ids([[(4 * t + k) % 512 for k in range(K)] for t in range(T)])
+    out.append(("one rank's 512 experts share every token, 4 slots", R, E, K, S, 4, even))
+    out.append(("one rank's 512 experts share every token, 256 slots", R, E, K, S, 256, even))
     return out

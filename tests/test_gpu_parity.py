@@ -123,6 +123,7 @@ CASES = [
     (4, 8, 2, 300, 256, 8, 3.0),       # the largest slot budget
     (64, 64, 4, 16, 1, 8, 5.0),        # 64 ranks, one expert and one slot each
     (4, 16, 2, 64, 4, 16384, 2.0),     # 32 KB rows
+    (16, 64, 4, 100, 128, 8, 3.0),     # R*slots = 2048 slot entries
     (4, 16, 3, 40, 4, 8200, 3.0),      # 1025 vectors per row: no thread shape fits exactly
 ]
 
