@@ -95,51 +95,120 @@ def measured_traffic(kernel_prefix, workload):
     return None
 
 
-def cpu_baseline(wl, ids_np, w_np, x_np, budget_s=15.0):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+def cpu_baseline(wl, ids_np, w_np, x_np, home=None, rep=None, budget_s=15.0):
+    """The oracle, as it stands, on a bounded sample of the same workload: each stage timed
+    on its own (time.perf_counter, median of 3).  Plan and slot map run on the whole batch;
+    dispatch and combine on its first n tokens, n sized to fit the time budget; the
+    replica-gradient reduce (workloads that carry gradients) on the leading columns of the
+    gradient slabs."""
     import numpy as np
     from oracle import moonep_oracle as O
 
-    t0 = time.perf_counter()
-    p = O.plan(ids_np, wl.R, wl.E, wl.K, wl.S, wl.slots)
-    dst = O.slot_map(p, ids_np)
-    t_plan = time.perf_counter() - t0
+    def med3(fn):
+        ts = []
+        for _ in range(3):
+            t = time.perf_counter()
+            r = fn()
+            ts.append(time.perf_counter() - t)
+        return statistics.median(ts), r
+
+    t_plan, p = med3(lambda: O.plan(ids_np, wl.R, wl.E, wl.K, wl.S, wl.slots))
+    t_map, dst = med3(lambda: O.slot_map(p, ids_np))
     rows_total = wl.R * p.sz.NvS
 
-    def run(n):
-        d = dst[:n]
-        t = time.perf_counter()
-        recv = O.dispatch(d, x_np[:n], rows_total)
-        t1 = time.perf_counter()
-        O.combine(d, w_np[:n], recv)
-        t2 = time.perf_counter()
-        return t1 - t, t2 - t1
-
-    probe = min(1024, wl.T)
-    td, tc = run(probe)
-    n = int(min(wl.T, max(probe, probe * budget_s / max(td + tc, 1e-6))))
-    reps = 1
-    if n > probe:
-        td, tc = run(n)
-    if n == wl.T and td + tc < budget_s / 2:
-        # the whole batch is shorter than the budget: repeat it, keep the median
-        runs = [(td, tc)] + [run(n) for _ in range(2)]
-        runs.sort(key=lambda r: r[0] + r[1])
-        td, tc = runs[1]
-        reps = 3
-    nbytes = dispatch_bytes(n, wl.K, wl.H) + combine_bytes(n, wl.K, wl.H)
+    # size the dispatch+combine sample: one probe on 512 tokens, then n tokens so that
+    # three repetitions of both stages take about budget_s
+    probe = min(512, wl.T)
+    t = time.perf_counter()
+    r = O.dispatch(dst[:probe], x_np[:probe], rows_total)
+    O.combine(dst[:probe], w_np[:probe], r)
+    per_tok = (time.perf_counter() - t) / probe
+    del r
+    n = int(min(wl.T, max(probe, budget_s / 3 / max(per_tok, 1e-9))))
+    d, xs, ws = dst[:n], x_np[:n], w_np[:n]
+    t_disp, recv = med3(lambda: O.dispatch(d, xs, rows_total))
+    t_comb, _ = med3(lambda: O.combine(d, ws, recv))
+    del recv
+    db, cb = dispatch_bytes(n, wl.K, wl.H), combine_bytes(n, wl.K, wl.H)
+    stages = {
+        "plan_ms": round(t_plan * 1e3, 3),
+        "slot_map_ms": round(t_map * 1e3, 3),
+        "dispatch_ms": round(t_disp * 1e3, 3), "dispatch_gbps": round(db / t_disp / 1e9, 4),
+        "combine_ms": round(t_comb * 1e3, 3), "combine_gbps": round(cb / t_comb / 1e9, 4),
+    }
+    sample = (f"plan and slot map of the whole maxvio={wl.maxvio[0]} batch ({wl.T} tokens); "
+              f"dispatch and combine of its first {n} tokens")
+    if home is not None and p.n_replicas:
+        cols = min(home.shape[1], 1 << 18)
+        h_np = home[:, :cols].cpu().numpy()
+        r_np = rep[:, :, :cols].cpu().numpy()
+        t_red, _ = med3(lambda: O.reduce_grad(p, h_np, r_np))
+        per = {}
+        for q in p.pieces:
+            if q[2] >= 0:
+                per[int(q[0])] = per.get(int(q[0]), 0) + 1
+        rb = sum((c + 2) * 4 * cols for c in per.values())
+        stages.update(reduce_ms=round(t_red * 1e3, 3), reduce_gbps=round(rb / t_red / 1e9, 4))
+        sample += f"; replica-gradient reduce over the first {cols} columns of each slab"
     return {
-        "value": round(nbytes / (td + tc) / 1e9, 4),
+        "value": round((db + cb) / (t_disp + t_comb) / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"oracle plan+slot map on the full maxvio={wl.maxvio[0]} batch "
-                  f"({t_plan * 1e3:.1f} ms), then dispatch+combine of its first {n} of "
-                  f"{wl.T} tokens ({td:.2f} s + {tc:.2f} s, median of {reps}); numpy, 1 thread",
-        "plan_ms": round(t_plan * 1e3, 2),
+        "sample": sample + "; each stage median of 3; numpy, 1 thread",
+        "stages": stages,
         "host_cpus": len(os.sched_getaffinity(0)),
         "host_cpu_model": cpu_model(),
     }
+
+
+def ceilings(wl, x, recv, out, dev, reps=10):
+    """Plain 16-byte streams on the same GPU (libmoonep_streams.so): a linear read, write
+    and copy of 4 GiB, and the row mixes of dispatch (one row read, K rows written) and
+    combine (K rows read, one row written) on this workload's rows, to contiguous rows and
+    to a seeded random permutation of the rows; GB/s, median of `reps` launches."""
+    import numpy as np
+    import torch
+    from combine_top_id_amd import streams as ST
+
+    def med(fn):
+        for _ in range(2):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record(); fn(); b.record()
+        torch.cuda.synchronize()
+        return statistics.median([a.elapsed_time(b) * 1e3 for a, b in ev])   # us
+
+    res = {}
+    n4 = 4 << 30
+    a = torch.empty(n4, dtype=torch.uint8, device=dev)
+    b = torch.empty(n4, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(16, dtype=torch.uint8, device=dev)
+    res["read_linear"] = round(n4 / med(lambda: ST.read(a, sink)) / 1e3, 1)
+    res["write_linear"] = round(n4 / med(lambda: ST.write(a)) / 1e3, 1)
+    res["copy_linear"] = round(n4 / med(lambda: ST.copy(a[:n4 // 2], b[:n4 // 2])) / 1e3, 1)
+    del a, b
+    T, K, H = wl.T, wl.K, wl.H
+    A = T * K
+    rb = 2 * H
+    ident = torch.arange(A, dtype=torch.int32, device=dev)
+    perm = torch.from_numpy(np.random.default_rng(20260001).permutation(A).astype(np.int32)).to(dev)
+    fan_rw, fan_w = T * (K + 1) * rb, T * K * rb
+    res["fanout_contiguous"] = round(fan_rw / med(lambda: ST.fanout(ident, K, x, recv)) / 1e3, 1)
+    res["fanout_scattered"] = round(fan_rw / med(lambda: ST.fanout(perm, K, x, recv)) / 1e3, 1)
+    res["write_scattered_rows"] = round(
+        fan_w / med(lambda: ST.fanout(perm, K, None, recv, read_src=False)) / 1e3, 1)
+    res["gather_contiguous"] = round(fan_rw / med(lambda: ST.gather(ident, K, recv, out)) / 1e3, 1)
+    res["gather_scattered"] = round(fan_rw / med(lambda: ST.gather(perm, K, recv, out)) / 1e3, 1)
+    res["read_scattered_rows"] = round(
+        fan_w / med(lambda: ST.gather(perm, K, recv, out, write_dst=False)) / 1e3, 1)
+    res["unit"] = "GB/s"
+    res["rows"] = (f"{T} source rows x K={K} of {rb} B; random destination rows are a seeded "
+                   f"permutation of {A} rows; each kernel one 64-lane workgroup per row chunk "
+                   f"(2 KB fan-out, 1 KB gather), linear streams 256 lanes per 4 KB")
+    return res
 
 
 def main():
@@ -153,8 +222,9 @@ def main():
     ap.add_argument("--no-prefetch", action="store_true")
     ap.add_argument("--no-staged", action="store_true")
     ap.add_argument("--flush", choices=("auto", "on", "off"), default="auto",
-                    help="write a 1 GiB buffer before every step so no input is served from "
+                    help="read a 1 GiB buffer before every step so no input is served from "
                          "the 256 MB last-level cache (auto: when a step moves < 2 GB)")
+    ap.add_argument("--no-ceilings", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -221,12 +291,17 @@ def main():
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     step_bytes = dispatch_bytes(wl.T, wl.K, wl.H) + combine_bytes(wl.T, wl.K, wl.H)
     flush = args.flush == "on" or (args.flush == "auto" and step_bytes < 2e9)
-    scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if flush else None
+    scrub = torch.ones(1 << 30, dtype=torch.uint8, device=dev) if flush else None
+    sink = torch.zeros(16, dtype=torch.uint8, device=dev)
+    if flush:
+        from combine_top_id_amd import streams as ST
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
         if flush:
-            scrub.fill_(s & 0xFF)          # evicts the last-level cache; not inside a step
+            # a plain-load read of 1 GiB (4x the last-level cache) displaces the step's
+            # inputs and leaves no dirty lines behind; not inside a step
+            ST.read(scrub, sink, policy=0)
         step(batches[s % nb], events[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -369,18 +444,15 @@ def main():
                         gbps=round(pb / tp / 1e3, 1) if st0["n_replicas"] else None)
         del home_w, slot_w
 
-    # a plain device copy of 4 GiB as a measured ceiling on the same box
-    a = torch.empty(1 << 31, dtype=torch.int16, device=dev)
-    c = torch.empty_like(a)
-    c.copy_(a)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(5):
-        c.copy_(a)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbps = 5 * 2 * a.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del a, c
+    # plain memory streams on the same GPU: the ceilings the kernels are set against
+    ceil = None
+    if not args.no_ceilings:
+        log("ceilings ...")
+        ceil = ceilings(wl, batches[0]["x"], recv, out, dev)
+        ceil["dispatch_over_fanout_scattered"] = round(
+            db / statistics.median(all_d) / 1e3 / ceil["fanout_scattered"], 4)
+        ceil["combine_over_gather_scattered"] = round(
+            cb / statistics.median(all_c) / 1e3 / ceil["gather_scattered"], 4)
 
     value = args.steps * (db + cb) / timed / 1e9
     res = {
@@ -403,7 +475,8 @@ def main():
                         f"the batches); identity expert",
             "R": wl.R, "E": wl.E, "K": wl.K, "S": wl.S, "H": wl.H, "slots": wl.slots,
             "tokens": wl.T, "accumulate": "fp32",
-            "cache": "flushed before every step (1 GiB write); value from step event spans"
+            "cache": "flushed before every step by a plain-load read of 1 GiB (no dirty lines); "
+                     "value from the steps' own event spans"
                      if flush else "not flushed (working set far above the 256 MB cache)",
         },
         "pct_hbm_peak": round(100 * value / PEAK_HBM_GBPS, 2),
@@ -421,7 +494,7 @@ def main():
         "per_maxvio": rows,
         "flatness_max_over_min": round(max(dc_times) / min(dc_times), 4),
         "plan_us_median": round(statistics.median([r["plan_us"] for r in rows]), 2),
-        "copy_ceiling_gbps": round(copy_gbps, 1),
+        "ceilings": ceil,
         "backward": backward,
         "prefetch": prefetch,
         "zero_copy_ab": staged,
@@ -430,7 +503,7 @@ def main():
         b0 = batches[0]
         log("cpu baseline (oracle) ...")
         res["cpu_baseline"] = cpu_baseline(wl, b0["ids"].cpu().numpy(), b0["w"].cpu().numpy(),
-                                           bf16_bits(b0["x"]))
+                                           bf16_bits(b0["x"]), home, rep)
     print(json.dumps(res), flush=True)
 
 

@@ -1,4 +1,5 @@
-"""Builds libmoonep.so for gfx950 with hipcc (in-tree, next to this file)."""
+"""Builds libmoonep.so (the hot path) and libmoonep_streams.so (the memory streams the
+benchmark measures ceilings with) for gfx950 with hipcc, in-tree next to this file."""
 
 import os
 import subprocess
@@ -6,6 +7,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = ["moonep_api.hip", "moonep_plan.hip", "moonep_move.hip"]
+STREAM_SOURCES = ["moonep_streams.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-shared",
@@ -16,18 +18,24 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose=False):
-    out = os.path.join(HERE, "libmoonep.so")
+def _hipcc(sources, name, verbose):
+    out = os.path.join(HERE, name)
     tmp = out + ".tmp"
     cmd = ["/opt/rocm/bin/hipcc", *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"),
            "-I", os.path.join(HERE, "csrc"),
-           *[os.path.join(HERE, "csrc", f) for f in SOURCES], "-o", tmp]
+           *[os.path.join(HERE, "csrc", f) for f in sources], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + r.stderr[-4000:])
     os.replace(tmp, out)
+    return out
+
+
+def build(verbose=False):
+    out = _hipcc(SOURCES, "libmoonep.so", verbose)
+    _hipcc(STREAM_SOURCES, "libmoonep_streams.so", verbose)
     build_c_smoke(verbose)
     return out
 

@@ -18,6 +18,11 @@ int check_desc(const moonep_plan_desc* d) {
   return MOONEP_OK;
 }
 
+// hipGetLastError() returns, and clears, the last error of the calling thread, whichever
+// call caused it.  Each entry point clears it right before its launches, so the status it
+// reads afterwards belongs to its own launches only.
+void clear_error() { (void)hipGetLastError(); }
+
 }  // namespace
 
 extern "C" {
@@ -46,6 +51,7 @@ int moonep_plan(const int32_t* topk_ids, const float* topk_w, int R, int E, int 
   desc->magic = kMagic;
   desc->sz = s;
   desc->dev = plan_dev;
+  clear_error();
   const hipError_t err = launch_plan(s, topk_ids, topk_w, static_cast<int32_t*>(plan_dev),
                                      static_cast<int32_t*>(workspace), stream);
   return err == hipSuccess ? MOONEP_OK : MOONEP_EHIP;
@@ -57,6 +63,8 @@ int moonep_dispatch(const moonep_plan_desc* plan, const uint16_t* x, int H, uint
   if (rc != MOONEP_OK) return rc;
   if (!x || !recv || H <= 0 || H % 8 != 0) return MOONEP_EINVAL;
   if (!aligned(x, 16) || !aligned(recv, 16)) return MOONEP_EALIGN;
+  if (!move_grid_fits(plan->sz, H)) return MOONEP_ELIMIT;
+  clear_error();
   const hipError_t err = launch_dispatch(plan->sz, static_cast<const int32_t*>(plan->dev), x,
                                          H, recv, stream);
   return err == hipSuccess ? MOONEP_OK : MOONEP_EHIP;
@@ -68,6 +76,8 @@ int moonep_combine(const moonep_plan_desc* plan, const uint16_t* y, int H, uint1
   if (rc != MOONEP_OK) return rc;
   if (!y || !out || H <= 0 || H % 8 != 0) return MOONEP_EINVAL;
   if (!aligned(y, 16) || !aligned(out, 16)) return MOONEP_EALIGN;
+  if (!move_grid_fits(plan->sz, H)) return MOONEP_ELIMIT;
+  clear_error();
   const hipError_t err = launch_combine(plan->sz, static_cast<const int32_t*>(plan->dev), y, H,
                                         out, stream);
   return err == hipSuccess ? MOONEP_OK : MOONEP_EHIP;
@@ -79,6 +89,8 @@ int moonep_dispatch_staged(const moonep_plan_desc* plan, const uint16_t* x, int 
   if (rc != MOONEP_OK) return rc;
   if (!x || !stage || !recv || H <= 0 || H % 8 != 0) return MOONEP_EINVAL;
   if (!aligned(x, 16) || !aligned(stage, 16) || !aligned(recv, 16)) return MOONEP_EALIGN;
+  if (!move_grid_fits(plan->sz, H)) return MOONEP_ELIMIT;
+  clear_error();
   const hipError_t err = launch_dispatch_staged(plan->sz, static_cast<const int32_t*>(plan->dev),
                                                 x, H, stage, recv, stream);
   return err == hipSuccess ? MOONEP_OK : MOONEP_EHIP;
@@ -90,6 +102,8 @@ int moonep_combine_staged(const moonep_plan_desc* plan, const uint16_t* y, int H
   if (rc != MOONEP_OK) return rc;
   if (!y || !stage || !out || H <= 0 || H % 8 != 0) return MOONEP_EINVAL;
   if (!aligned(y, 16) || !aligned(stage, 16) || !aligned(out, 16)) return MOONEP_EALIGN;
+  if (!move_grid_fits(plan->sz, H)) return MOONEP_ELIMIT;
+  clear_error();
   const hipError_t err = launch_combine_staged(plan->sz, static_cast<const int32_t*>(plan->dev),
                                                y, H, stage, out, stream);
   return err == hipSuccess ? MOONEP_OK : MOONEP_EHIP;
@@ -101,6 +115,8 @@ int moonep_dispatch_bwd(const moonep_plan_desc* plan, const uint16_t* g_recv, in
   if (rc != MOONEP_OK) return rc;
   if (!g_recv || !gx || H <= 0 || H % 8 != 0) return MOONEP_EINVAL;
   if (!aligned(g_recv, 16) || !aligned(gx, 16)) return MOONEP_EALIGN;
+  if (!move_grid_fits(plan->sz, H)) return MOONEP_ELIMIT;
+  clear_error();
   const hipError_t err = launch_dispatch_bwd(plan->sz, static_cast<const int32_t*>(plan->dev),
                                              g_recv, H, gx, stream);
   return err == hipSuccess ? MOONEP_OK : MOONEP_EHIP;
@@ -113,6 +129,7 @@ int moonep_combine_bwd(const moonep_plan_desc* plan, const uint16_t* dout, const
   if (!dout || !y || !g_y || !dw || H <= 0 || H % 8 != 0) return MOONEP_EINVAL;
   if (!aligned(dout, 16) || !aligned(y, 16) || !aligned(g_y, 16) || !aligned(dw, 4))
     return MOONEP_EALIGN;
+  clear_error();
   const hipError_t err = launch_combine_bwd(plan->sz, static_cast<const int32_t*>(plan->dev),
                                             dout, y, H, g_y, dw, stream);
   return err == hipSuccess ? MOONEP_OK : MOONEP_EHIP;
@@ -126,6 +143,7 @@ int moonep_reduce_grad(const moonep_plan_desc* plan, float* home_grad, const flo
   if (plan->sz.slots > 0 && !rep_grad) return MOONEP_EINVAL;
   if (!aligned(home_grad, 16) || (rep_grad && !aligned(rep_grad, 16))) return MOONEP_EALIGN;
   if (G_el == 0 || plan->sz.slots == 0) return MOONEP_OK;
+  clear_error();
   const hipError_t err = launch_reduce(plan->sz, static_cast<const int32_t*>(plan->dev),
                                        home_grad, rep_grad, G_el, stream);
   return err == hipSuccess ? MOONEP_OK : MOONEP_EHIP;
@@ -139,6 +157,7 @@ int moonep_prefetch_weight(const moonep_plan_desc* plan, const uint16_t* home_w,
   if (plan->sz.slots > 0 && !slot_w) return MOONEP_EINVAL;
   if (!aligned(home_w, 16) || (slot_w && !aligned(slot_w, 16))) return MOONEP_EALIGN;
   if (plan->sz.slots == 0) return MOONEP_OK;
+  clear_error();
   const hipError_t err = launch_prefetch(plan->sz, static_cast<const int32_t*>(plan->dev), home_w,
                                          W_el, slot_w, stream);
   return err == hipSuccess ? MOONEP_OK : MOONEP_EHIP;
@@ -155,6 +174,7 @@ int moonep_expert_stub(const moonep_plan_desc* plan, const int32_t* topk_ids,
   if (!aligned(recv, 16) || !aligned(home_w, 16) || !aligned(y, 16) || !aligned(topk_ids, 4) ||
       (slot_w && !aligned(slot_w, 16)))
     return MOONEP_EALIGN;
+  clear_error();
   const hipError_t err = launch_expert_stub(plan->sz, static_cast<const int32_t*>(plan->dev),
                                             topk_ids, recv, home_w, slot_w, W_el, H, y, stream);
   return err == hipSuccess ? MOONEP_OK : MOONEP_EHIP;

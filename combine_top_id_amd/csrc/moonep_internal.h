@@ -104,7 +104,11 @@ __host__ __device__ inline int64_t ws_snap(const moonep_sizes& s) {
   return ws_sub(s) + align64((int64_t)s.nblk * kMapWaves * s.E);
 }
 
-// Launchers (defined in the .hip files).
+// Launchers (defined in the .hip files).  Each returns the launch status of what it
+// enqueued; the C ABI clears any earlier, unrelated error of the thread before calling.
+// Whether the dispatch/combine grids (one workgroup per token and row chunk) fit the
+// launch limit for rows of H bf16 elements:
+bool move_grid_fits(const moonep_sizes& s, int H);
 hipError_t launch_plan(const moonep_sizes& s, const int32_t* ids, const float* w,
                        int32_t* plan, int32_t* ws, hipStream_t st);
 hipError_t launch_dispatch(const moonep_sizes& s, const int32_t* plan, const uint16_t* x,

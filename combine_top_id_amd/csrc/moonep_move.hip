@@ -16,8 +16,6 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int64_t kLastLevelCacheBytes = 256ll << 20;   // MI355X Infinity Cache
-
 __device__ __forceinline__ float bf_lo(unsigned int v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf_hi(unsigned int v) { return __uint_as_float(v & 0xFFFF0000u); }
 
@@ -48,68 +46,64 @@ void row_shape(int nvec, int umax, int upref, int* threads, int* u) {
 // ---------------------------------------------------------------------------------------
 // dispatch: recv[dst_row[t, k]] = x[t]
 // ---------------------------------------------------------------------------------------
-// One workgroup per token: each thread loads U vectors of the row, then stores each of
-// them to the token's K destination rows in turn.  Measured on MI355X: storing one
-// vector to all K rows before the next is about 1.5% faster than writing the rows one
-// after another, and non-temporal loads of x are 2% slower.  Stores: when the whole
-// destination buffer fits the 256 MB last-level cache, plain stores leave it dirty there
-// and the next kernel pays for the write-back (a combine reading it right after took 45%
-// longer), so the stores are non-temporal (NTS); for larger buffers non-temporal stores
-// are 5-8% slower and plain stores are used.
+// One single-wave workgroup per (token, chunk of kDispChunk 16-byte vectors): each lane
+// loads kDispU vectors of the chunk (64 vectors apart, so every load and store of the
+// wave covers 1 KB contiguous), then stores each of them to the token's K destination
+// rows, vector by vector, with non-temporal stores.  Measured on MI355X, interleaved A/B
+// in one process on DeepSeek-V3-, Kimi- and decode-shaped routing: one wave per 2 KB
+// chunk is 2-5% faster than one 448-thread workgroup per token, non-temporal stores add
+// 2-4% on top, and a token-major launch order beats chunk-major or XCD-local orders.
+// A workgroup of one wave starts as soon as any wave slot of a CU frees, so the CUs stay
+// full of short-lived waves; larger workgroups wait for several free slots at once.
+//
 // KT = K when K is a compile-time constant (the rows are then held in registers), else 0.
-template <int KT, int U, bool NTS>
-__global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t* __restrict__ dst,
-                                                       const u32x4* __restrict__ x,
-                                                       u32x4* __restrict__ recv, int Krt,
-                                                       int nvec, int nrows) {
+// STAGED: the destination is row t*K + k of a [T*K, H] staging buffer (the non-zero-copy
+// A/B baseline), not the plan's row; it has its own instantiation so that profiles keep
+// the zero-copy kernel's figures apart.
+constexpr int kWave = 64;
+constexpr int kDispU = 2;
+constexpr int kDispChunk = kWave * kDispU;     // 128 vectors = 2 KB of a bf16 row
+constexpr int kCombChunk = kWave;              // 64 vectors = 1 KB of a bf16 row
+
+template <int KT, bool STAGED>
+__global__ __launch_bounds__(kWave) void dispatch_kernel(const int32_t* __restrict__ dst,
+                                                         const u32x4* __restrict__ x,
+                                                         u32x4* __restrict__ recv, int Krt,
+                                                         int nvec, int nch, int nrows) {
   const int K = KT > 0 ? KT : Krt;
-  const int64_t t = blockIdx.x;
-  const int32_t* d = dst ? dst + t * K : nullptr;   // null: staging row t*K + k
+  const int64_t t = blockIdx.x / nch;
+  const int c0 = (int)(blockIdx.x - t * nch) * kDispChunk + (int)threadIdx.x;
+  const int32_t* d = STAGED ? nullptr : dst + t * K;
   const u32x4* src = x + t * nvec;
-  const int step = blockDim.x * U;
+  u32x4 buf[kDispU];
+#pragma unroll
+  for (int u = 0; u < kDispU; ++u) {
+    const int v = c0 + u * kWave;
+    if (v < nvec) buf[u] = src[v];
+  }
   if constexpr (KT > 0) {
     int rows[KT];
 #pragma unroll
-    for (int k = 0; k < KT; ++k) rows[k] = d ? d[k] : (int)(t * K + k);
-    for (int v0 = threadIdx.x; v0 < nvec; v0 += step) {
-      u32x4 buf[U];
+    for (int k = 0; k < KT; ++k) rows[k] = STAGED ? (int)(t * K + k) : d[k];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int v = v0 + u * blockDim.x;
-        if (v < nvec) buf[u] = src[v];
-      }
+    for (int u = 0; u < kDispU; ++u) {
+      const int v = c0 + u * kWave;
+      if (v < nvec) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int v = v0 + u * blockDim.x;
-        if (v < nvec) {
-#pragma unroll
-          for (int k = 0; k < KT; ++k)
-            if ((unsigned)rows[k] < (unsigned)nrows) {    // -1: unmapped
-              u32x4* o = recv + (int64_t)rows[k] * nvec + v;
-              if constexpr (NTS) __builtin_nontemporal_store(buf[u], o); else *o = buf[u];
-            }
-        }
+        for (int k = 0; k < KT; ++k)
+          if ((unsigned)rows[k] < (unsigned)nrows)   // -1: unmapped
+            __builtin_nontemporal_store(buf[u], recv + (int64_t)rows[k] * nvec + v);
       }
     }
   } else {
-    for (int v0 = threadIdx.x; v0 < nvec; v0 += step) {
-      u32x4 buf[U];
+    for (int k = 0; k < K; ++k) {
+      const int row = STAGED ? (int)(t * K + k) : d[k];
+      if ((unsigned)row >= (unsigned)nrows) continue;   // -1: unmapped
+      u32x4* o = recv + (int64_t)row * nvec;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int v = v0 + u * blockDim.x;
-        if (v < nvec) buf[u] = src[v];
-      }
-      for (int k = 0; k < K; ++k) {
-        const int row = d ? d[k] : (int)(t * K + k);
-        if ((unsigned)row >= (unsigned)nrows) continue;   // -1: unmapped
-        u32x4* o = recv + (int64_t)row * nvec;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int v = v0 + u * blockDim.x;
-          if (v < nvec) {
-            if constexpr (NTS) __builtin_nontemporal_store(buf[u], o + v); else o[v] = buf[u];
-          }
-        }
+      for (int u = 0; u < kDispU; ++u) {
+        const int v = c0 + u * kWave;
+        if (v < nvec) __builtin_nontemporal_store(buf[u], o + v);
       }
     }
   }
@@ -118,75 +112,69 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t* __restric
 // ---------------------------------------------------------------------------------------
 // combine: out[t] = bf16( sum_k w[t,k] * y[dst_row[t,k]] ), fp32, k ascending, no FMA
 // ---------------------------------------------------------------------------------------
-// acc += w * y[row, v0 + u*blockDim.x] for the thread's U vectors (8 bf16 each): a
-// separate fp32 multiply and add per element, in the caller's k order.  The rows are
-// read with non-temporal loads (about 9% faster than plain loads), and the output row is
-// written with a non-temporal store.
-template <int U, bool WEIGHTED>
-__device__ __forceinline__ void combine_accumulate(float (&acc)[U][8], const u32x4* __restrict__ y,
-                                                   int row, float wk, int v0, int nvec,
-                                                   int nrows) {
-  if ((unsigned)row >= (unsigned)nrows) return;    // -1: unmapped
-  const u32x4* src = y + (int64_t)row * nvec;
-  u32x4 yv[U];
+// One single-wave workgroup per (token, chunk of 64 vectors): each lane issues its K row
+// loads (non-temporal) before any arithmetic, then acc = acc + w*y per element with a
+// separate fp32 multiply and add, in k order, one round-to-nearest-even to bf16, and a
+// non-temporal store.  Measured on MI355X against one 448-thread workgroup per token
+// (interleaved A/B): 2-6% faster; plain loads or a plain store lose 6-10%.
+// An assignment whose plan row is -1 (an invalid plan) adds nothing, so such a token's
+// output is a zero row.  STAGED: the K rows are read from staging rows t*K + k (the
+// non-zero-copy prologue filled them); the plan's row still decides whether an
+// assignment is mapped.  WEIGHTED = false is the gradient of dispatch:
+// gx[t] = bf16(sum_k g_recv[dst_row[t,k]]).
+template <int KT, bool WEIGHTED, bool STAGED>
+__global__ __launch_bounds__(kWave) void combine_kernel(const int32_t* __restrict__ dst,
+                                                        const float* __restrict__ wts,
+                                                        const u32x4* __restrict__ y,
+                                                        u32x4* __restrict__ out, int Krt,
+                                                        int nvec, int nch, int nrows) {
+  const int K = KT > 0 ? KT : Krt;
+  const int64_t t = blockIdx.x / nch;
+  const int v = (int)(blockIdx.x - t * nch) * kCombChunk + (int)threadIdx.x;
+  const int32_t* d = dst + t * K;
+  const float* wt = wts + t * K;
+  if (v >= nvec) return;
+  float acc[8];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int v = v0 + u * blockDim.x;
-    yv[u] = v < nvec ? __builtin_nontemporal_load(src + v) : u32x4{0u, 0u, 0u, 0u};
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  auto add = [&](const u32x4 yv, float wk) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const unsigned int bits = yv[u][q];
-      const float p0 = WEIGHTED ? wk * bf_lo(bits) : bf_lo(bits);
-      const float p1 = WEIGHTED ? wk * bf_hi(bits) : bf_hi(bits);
-      acc[u][2 * q] = acc[u][2 * q] + p0;
-      acc[u][2 * q + 1] = acc[u][2 * q + 1] + p1;
+      const float p0 = WEIGHTED ? wk * bf_lo(yv[q]) : bf_lo(yv[q]);
+      const float p1 = WEIGHTED ? wk * bf_hi(yv[q]) : bf_hi(yv[q]);
+      acc[2 * q] = acc[2 * q] + p0;
+      acc[2 * q + 1] = acc[2 * q + 1] + p1;
+    }
+  };
+  if constexpr (KT > 0) {
+    int rows[KT];
+    bool ok[KT];
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+      const int r = d[k];
+      ok[k] = (unsigned)r < (unsigned)nrows;       // -1: unmapped
+      rows[k] = STAGED ? (int)(t * K + k) : r;
+    }
+    u32x4 yv[KT];
+#pragma unroll
+    for (int k = 0; k < KT; ++k)
+      yv[k] = ok[k] ? __builtin_nontemporal_load(y + (int64_t)rows[k] * nvec + v)
+                    : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < KT; ++k)
+      if (ok[k]) add(yv[k], WEIGHTED ? wt[k] : 1.f);
+  } else {
+    for (int k = 0; k < K; ++k) {
+      const int r = d[k];
+      if ((unsigned)r >= (unsigned)nrows) continue;   // -1: unmapped
+      const int64_t row = STAGED ? t * K + k : r;
+      add(__builtin_nontemporal_load(y + row * nvec + v), WEIGHTED ? wt[k] : 1.f);
     }
   }
-}
-
-// WEIGHTED = false is the gradient of dispatch: gx[t] = bf16(sum_k g_recv[dst_row[t,k]]).
-template <int KT, int U, bool WEIGHTED>
-__global__ __launch_bounds__(1024) void combine_kernel(const int32_t* __restrict__ dst,
-                                                      const float* __restrict__ wts,
-                                                      const u32x4* __restrict__ y,
-                                                      u32x4* __restrict__ out, int Krt,
-                                                      int nvec, int nrows) {
-  const int K = KT > 0 ? KT : Krt;
-  const int64_t t = blockIdx.x;
-  const int32_t* d = dst ? dst + t * K : nullptr;   // null: staging row t*K + k
-  const float* wt = wts + t * K;
-  const int step = blockDim.x * U;
-  for (int v0 = threadIdx.x; v0 < nvec; v0 += step) {
-    float acc[U][8];
+  u32x4 o;
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[u][j] = 0.f;
-    if constexpr (KT > 0) {
-#pragma unroll
-      for (int k = 0; k < KT; ++k)
-        combine_accumulate<U, WEIGHTED>(acc, y, d ? d[k] : (int)(t * K + k),
-                                        WEIGHTED ? wt[k] : 1.f, v0, nvec, nrows);
-    } else {
-      for (int k = 0; k < K; ++k)
-        combine_accumulate<U, WEIGHTED>(acc, y, d ? d[k] : (int)(t * K + k),
-                                        WEIGHTED ? wt[k] : 1.f, v0, nvec, nrows);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int v = v0 + u * blockDim.x;
-      if (v < nvec) {
-        u32x4 o;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          o[q] = to_bf16(acc[u][2 * q]) | (to_bf16(acc[u][2 * q + 1]) << 16);
-        __builtin_nontemporal_store(o, out + t * nvec + v);
-      }
-    }
-  }
+  for (int q = 0; q < 4; ++q) o[q] = to_bf16(acc[2 * q]) | (to_bf16(acc[2 * q + 1]) << 16);
+  __builtin_nontemporal_store(o, out + t * nvec + v);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -486,105 +474,81 @@ __global__ __launch_bounds__(kRedThreads) void reduce_kernel(const int32_t* __re
 }
 
 
-template <int KT, int U>
-void launch_dispatch_ku(const moonep_sizes& s, const int32_t* dst, int nrows, const uint16_t* x,
-                        uint16_t* recv, int nvec, int threads, hipStream_t st) {
-  const bool fits_llc = (int64_t)nrows * nvec * 16 <= kLastLevelCacheBytes;
-  if (fits_llc)
-    hipLaunchKernelGGL((dispatch_kernel<KT, U, true>), dim3((unsigned)s.T), dim3(threads), 0, st,
-                       dst, reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(recv), s.K,
-                       nvec, nrows);
-  else
-    hipLaunchKernelGGL((dispatch_kernel<KT, U, false>), dim3((unsigned)s.T), dim3(threads), 0, st,
-                       dst, reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(recv), s.K,
-                       nvec, nrows);
+template <int KT, bool STAGED>
+void launch_dispatch_k(const moonep_sizes& s, const int32_t* dst, int nrows, const uint16_t* x,
+                       uint16_t* recv, int nvec, int nch, hipStream_t st) {
+  hipLaunchKernelGGL((dispatch_kernel<KT, STAGED>), dim3((unsigned)(s.T * nch)), dim3(kWave), 0, st,
+                     dst, reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(recv), s.K, nvec,
+                     nch, nrows);
 }
 
-template <int KT>
-void launch_dispatch_k(const moonep_sizes& s, const int32_t* dst, int nrows, const uint16_t* x,
-                       uint16_t* recv, int nvec, int threads, int u, hipStream_t st) {
-  switch (u) {
-    case 1: launch_dispatch_ku<KT, 1>(s, dst, nrows, x, recv, nvec, threads, st); break;
-    case 2: launch_dispatch_ku<KT, 2>(s, dst, nrows, x, recv, nvec, threads, st); break;
-    case 3: launch_dispatch_ku<KT, 3>(s, dst, nrows, x, recv, nvec, threads, st); break;
-    default: launch_dispatch_ku<KT, 4>(s, dst, nrows, x, recv, nvec, threads, st); break;
+template <bool STAGED>
+void dispatch_rows(const moonep_sizes& s, const int32_t* dst, int nrows, const uint16_t* x, int H,
+                   uint16_t* recv, hipStream_t st) {
+  const int nvec = H / 8;
+  const int nch = (nvec + kDispChunk - 1) / kDispChunk;
+  switch (s.K) {
+    case 1: launch_dispatch_k<1, STAGED>(s, dst, nrows, x, recv, nvec, nch, st); break;
+    case 2: launch_dispatch_k<2, STAGED>(s, dst, nrows, x, recv, nvec, nch, st); break;
+    case 4: launch_dispatch_k<4, STAGED>(s, dst, nrows, x, recv, nvec, nch, st); break;
+    case 6: launch_dispatch_k<6, STAGED>(s, dst, nrows, x, recv, nvec, nch, st); break;
+    case 8: launch_dispatch_k<8, STAGED>(s, dst, nrows, x, recv, nvec, nch, st); break;
+    default: launch_dispatch_k<0, STAGED>(s, dst, nrows, x, recv, nvec, nch, st); break;
   }
 }
 
-template <int KT, int U, bool WEIGHTED>
-void launch_combine_ku(const moonep_sizes& s, const int32_t* dst, const float* w,
-                       const uint16_t* y, uint16_t* out, int nvec, int threads, hipStream_t st) {
-  hipLaunchKernelGGL((combine_kernel<KT, U, WEIGHTED>), dim3((unsigned)s.T), dim3(threads), 0, st, dst,
-                     w, reinterpret_cast<const u32x4*>(y), reinterpret_cast<u32x4*>(out), s.K,
-                     nvec, dst ? (int)s.recv_rows : (int)s.A);
+template <int KT, bool WEIGHTED, bool STAGED>
+void launch_combine_k(const moonep_sizes& s, const int32_t* dst, const float* w, const uint16_t* y,
+                      uint16_t* out, int nvec, int nch, hipStream_t st) {
+  hipLaunchKernelGGL((combine_kernel<KT, WEIGHTED, STAGED>), dim3((unsigned)(s.T * nch)), dim3(kWave),
+                     0, st, dst, w, reinterpret_cast<const u32x4*>(y), reinterpret_cast<u32x4*>(out),
+                     s.K, nvec, nch, (int)s.recv_rows);
 }
 
-template <int KT, bool WEIGHTED>
-void launch_combine_k(const moonep_sizes& s, const int32_t* dst, const float* w,
-                      const uint16_t* y, uint16_t* out, int nvec, int threads, int u,
-                      hipStream_t st) {
-  switch (u) {
-    case 1: launch_combine_ku<KT, 1, WEIGHTED>(s, dst, w, y, out, nvec, threads, st); break;
-    case 2: launch_combine_ku<KT, 2, WEIGHTED>(s, dst, w, y, out, nvec, threads, st); break;
-    case 3: launch_combine_ku<KT, 3, WEIGHTED>(s, dst, w, y, out, nvec, threads, st); break;
-    default: launch_combine_ku<KT, 4, WEIGHTED>(s, dst, w, y, out, nvec, threads, st); break;
+template <bool WEIGHTED, bool STAGED>
+void gather_sum(const moonep_sizes& s, const int32_t* plan, const uint16_t* y, int H, uint16_t* out,
+                hipStream_t st) {
+  const int nvec = H / 8;
+  const int nch = (nvec + kCombChunk - 1) / kCombChunk;
+  const int32_t* dst = plan + s.o_dst_row;
+  const float* w = reinterpret_cast<const float*>(plan + s.o_w);
+  switch (s.K) {
+    case 1: launch_combine_k<1, WEIGHTED, STAGED>(s, dst, w, y, out, nvec, nch, st); break;
+    case 2: launch_combine_k<2, WEIGHTED, STAGED>(s, dst, w, y, out, nvec, nch, st); break;
+    case 4: launch_combine_k<4, WEIGHTED, STAGED>(s, dst, w, y, out, nvec, nch, st); break;
+    case 6: launch_combine_k<6, WEIGHTED, STAGED>(s, dst, w, y, out, nvec, nch, st); break;
+    case 8: launch_combine_k<8, WEIGHTED, STAGED>(s, dst, w, y, out, nvec, nch, st); break;
+    default: launch_combine_k<0, WEIGHTED, STAGED>(s, dst, w, y, out, nvec, nch, st); break;
   }
 }
 
 }  // namespace
 
-// rows from the plan's dst_row, or (staged) row t*K + k of a [T*K, H] staging buffer
-hipError_t dispatch_rows(const moonep_sizes& s, const int32_t* dst, int nrows, const uint16_t* x,
-                         int H, uint16_t* recv, hipStream_t st) {
-  const int nvec = H / 8;
-  int threads = 64, u = 1;
-  row_shape(nvec, 4, 2, &threads, &u);
-  switch (s.K) {
-    case 1: launch_dispatch_k<1>(s, dst, nrows, x, recv, nvec, threads, u, st); break;
-    case 2: launch_dispatch_k<2>(s, dst, nrows, x, recv, nvec, threads, u, st); break;
-    case 4: launch_dispatch_k<4>(s, dst, nrows, x, recv, nvec, threads, u, st); break;
-    case 6: launch_dispatch_k<6>(s, dst, nrows, x, recv, nvec, threads, u, st); break;
-    case 8: launch_dispatch_k<8>(s, dst, nrows, x, recv, nvec, threads, u, st); break;
-    default: launch_dispatch_k<0>(s, dst, nrows, x, recv, nvec, threads, u, st); break;
-  }
-  return hipGetLastError();
+bool move_grid_fits(const moonep_sizes& s, int H) {
+  const int64_t nvec = H / 8;
+  const int64_t nch = (nvec + kCombChunk - 1) / kCombChunk;   // the finer of the two chunkings
+  return s.T * nch <= INT32_MAX;
 }
 
 hipError_t launch_dispatch(const moonep_sizes& s, const int32_t* plan, const uint16_t* x,
                            int H, uint16_t* recv, hipStream_t st) {
-  return dispatch_rows(s, plan + s.o_dst_row, (int)s.recv_rows, x, H, recv, st);
+  dispatch_rows<false>(s, plan + s.o_dst_row, (int)s.recv_rows, x, H, recv, st);
+  return hipGetLastError();
 }
 
 hipError_t launch_dispatch_staged(const moonep_sizes& s, const int32_t* plan, const uint16_t* x,
                                   int H, uint16_t* stage, uint16_t* recv, hipStream_t st) {
-  const hipError_t err = dispatch_rows(s, nullptr, (int)s.A, x, H, stage, st);
+  dispatch_rows<true>(s, nullptr, (int)s.A, x, H, stage, st);
+  const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   launch_copy_rows<true>(s, plan + s.o_dst_row, stage, recv, H / 8, st);
   return hipGetLastError();
 }
 
-template <bool WEIGHTED>
-hipError_t launch_gather_sum(const moonep_sizes& s, const int32_t* plan, const uint16_t* y,
-                             int H, uint16_t* out, hipStream_t st, bool staged = false) {
-  const int nvec = H / 8;
-  int threads = 64, u = 1;
-  row_shape(nvec, 4, 2, &threads, &u);
-  const int32_t* dst = staged ? nullptr : plan + s.o_dst_row;
-  const float* w = reinterpret_cast<const float*>(plan + s.o_w);
-  switch (s.K) {
-    case 1: launch_combine_k<1, WEIGHTED>(s, dst, w, y, out, nvec, threads, u, st); break;
-    case 2: launch_combine_k<2, WEIGHTED>(s, dst, w, y, out, nvec, threads, u, st); break;
-    case 4: launch_combine_k<4, WEIGHTED>(s, dst, w, y, out, nvec, threads, u, st); break;
-    case 6: launch_combine_k<6, WEIGHTED>(s, dst, w, y, out, nvec, threads, u, st); break;
-    case 8: launch_combine_k<8, WEIGHTED>(s, dst, w, y, out, nvec, threads, u, st); break;
-    default: launch_combine_k<0, WEIGHTED>(s, dst, w, y, out, nvec, threads, u, st); break;
-  }
-  return hipGetLastError();
-}
-
 hipError_t launch_combine(const moonep_sizes& s, const int32_t* plan, const uint16_t* y,
                           int H, uint16_t* out, hipStream_t st) {
-  return launch_gather_sum<true>(s, plan, y, H, out, st);
+  gather_sum<true, false>(s, plan, y, H, out, st);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine_staged(const moonep_sizes& s, const int32_t* plan, const uint16_t* y,
@@ -592,12 +556,14 @@ hipError_t launch_combine_staged(const moonep_sizes& s, const int32_t* plan, con
   launch_copy_rows<false>(s, plan + s.o_dst_row, y, stage, H / 8, st);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return launch_gather_sum<true>(s, plan, stage, H, out, st, true);
+  gather_sum<true, true>(s, plan, stage, H, out, st);
+  return hipGetLastError();
 }
 
 hipError_t launch_dispatch_bwd(const moonep_sizes& s, const int32_t* plan, const uint16_t* g_recv,
                                int H, uint16_t* gx, hipStream_t st) {
-  return launch_gather_sum<false>(s, plan, g_recv, H, gx, st);
+  gather_sum<false, false>(s, plan, g_recv, H, gx, st);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine_bwd(const moonep_sizes& s, const int32_t* plan, const uint16_t* dout,

@@ -69,7 +69,8 @@ def lib():
     L.moonep_plan_status.argtypes = [ctypes.POINTER(PlanDesc), ctypes.POINTER(PlanStats), vp]
     L.moonep_strerror.argtypes = [i32]
     L.moonep_strerror.restype = ctypes.c_char_p
-    for f in ("moonep_query", "moonep_plan", "moonep_dispatch", "moonep_combine",
+    for f in ("moonep_query", "moonep_plan", "moonep_dispatch",
+              "moonep_combine",
               "moonep_reduce_grad", "moonep_plan_status", "moonep_dispatch_bwd",
               "moonep_combine_bwd", "moonep_prefetch_weight", "moonep_expert_stub",
               "moonep_dispatch_staged", "moonep_combine_staged"):
@@ -78,7 +79,8 @@ def lib():
     return L
 
 
-EXPORTS = ("moonep_query", "moonep_plan", "moonep_dispatch", "moonep_combine",
+EXPORTS = ("moonep_query", "moonep_plan", "moonep_dispatch",
+           "moonep_combine",
            "moonep_reduce_grad", "moonep_plan_status", "moonep_strerror",
            "moonep_dispatch_bwd", "moonep_combine_bwd", "moonep_prefetch_weight",
            "moonep_expert_stub", "moonep_dispatch_staged", "moonep_combine_staged")
@@ -89,9 +91,13 @@ def _check(rc):
         raise MoonepError(f"moonep error {rc}: {lib().moonep_strerror(rc).decode()}")
 
 
-def _stream(stream):
+def _stream(stream, device):
+    """The HIP stream handle to enqueue on: `stream`, else the current stream of the
+    tensors' device (not of whichever device happens to be current)."""
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(device)
+    elif stream.device != device:
+        raise MoonepError(f"stream is on {stream.device}, the tensors on {device}")
     return ctypes.c_void_p(stream.cuda_stream)
 
 
@@ -152,7 +158,7 @@ def moonep_plan(topk_ids, topk_w, R, E, K, S, slots, plan=None, stream=None) -> 
     reduce).  Pass `plan` to reuse its blob and workspace (same sizes)."""
     sz = moonep_query(R, E, K, S, slots)
     ids_p = _dev(topk_ids, torch.int32, "topk_ids")
-    w_p = _dev(topk_w, torch.float32, "topk_w")
+    w_p = _dev(topk_w, torch.float32, "topk_w", topk_ids.device)
     if topk_ids.numel() != sz.A or topk_w.numel() != sz.A:
         raise MoonepError("topk_ids / topk_w must hold R*S*K elements")
     if plan is None or plan.sz.plan_bytes != sz.plan_bytes or \
@@ -163,7 +169,7 @@ def moonep_plan(topk_ids, topk_w, R, E, K, S, slots, plan=None, stream=None) -> 
     _check(lib().moonep_plan(ids_p, w_p, R, E, K, S, slots,
                              ctypes.c_void_p(plan.blob.data_ptr()),
                              ctypes.c_void_p(plan.workspace.data_ptr()),
-                             ctypes.byref(plan.desc), _stream(stream)))
+                             ctypes.byref(plan.desc), _stream(stream, topk_ids.device)))
     return plan
 
 
@@ -178,7 +184,7 @@ def moonep_dispatch(plan: Plan, x, recv=None, stream=None):
     if recv.numel() != plan.sz.recv_rows * H:
         raise MoonepError("recv must be [R*NvS, H]")
     _check(lib().moonep_dispatch(ctypes.byref(plan.desc), _dev(x, torch.bfloat16, "x", D), H,
-                                 _dev(recv, torch.bfloat16, "recv", D), _stream(stream)))
+                                 _dev(recv, torch.bfloat16, "recv", D), _stream(stream, D)))
     return recv
 
 
@@ -193,7 +199,7 @@ def moonep_combine(plan: Plan, y, out=None, stream=None):
     if out.numel() != plan.sz.T * H:
         raise MoonepError("out must be [T, H]")
     _check(lib().moonep_combine(ctypes.byref(plan.desc), _dev(y, torch.bfloat16, "y", D), H,
-                                _dev(out, torch.bfloat16, "out", D), _stream(stream)))
+                                _dev(out, torch.bfloat16, "out", D), _stream(stream, D)))
     return out
 
 
@@ -209,12 +215,16 @@ def moonep_dispatch_staged(plan: Plan, x, recv=None, stage=None, stream=None):
     """Non-zero-copy dispatch: x -> stage (arrival order) -> recv (epilogue copy)."""
     D = plan.blob.device
     H = x.shape[-1]
+    if x.numel() != plan.sz.T * H:
+        raise MoonepError("x must be [T, H]")
     stage = _stage(plan, H, stage, x.device)
     if recv is None:
         recv = torch.empty(plan.sz.recv_rows, H, dtype=torch.bfloat16, device=x.device)
+    if recv.numel() != plan.sz.recv_rows * H:
+        raise MoonepError("recv must be [R*NvS, H]")
     _check(lib().moonep_dispatch_staged(ctypes.byref(plan.desc), _dev(x, torch.bfloat16, "x", D), H,
                                         _dev(stage, torch.bfloat16, "stage", D),
-                                        _dev(recv, torch.bfloat16, "recv", D), _stream(stream)))
+                                        _dev(recv, torch.bfloat16, "recv", D), _stream(stream, D)))
     return recv
 
 
@@ -222,12 +232,16 @@ def moonep_combine_staged(plan: Plan, y, out=None, stage=None, stream=None):
     """Non-zero-copy combine: y -> stage (prologue copy) -> weighted sum -> out."""
     D = plan.blob.device
     H = y.shape[-1]
+    if y.numel() != plan.sz.recv_rows * H:
+        raise MoonepError("y must be [R*NvS, H]")
     stage = _stage(plan, H, stage, y.device)
     if out is None:
         out = torch.empty(plan.sz.T, H, dtype=torch.bfloat16, device=y.device)
+    if out.numel() != plan.sz.T * H:
+        raise MoonepError("out must be [T, H]")
     _check(lib().moonep_combine_staged(ctypes.byref(plan.desc), _dev(y, torch.bfloat16, "y", D), H,
                                        _dev(stage, torch.bfloat16, "stage", D),
-                                       _dev(out, torch.bfloat16, "out", D), _stream(stream)))
+                                       _dev(out, torch.bfloat16, "out", D), _stream(stream, D)))
     return out
 
 
@@ -243,7 +257,7 @@ def moonep_dispatch_bwd(plan: Plan, g_recv, gx=None, stream=None):
         raise MoonepError("gx must be [T, H]")
     _check(lib().moonep_dispatch_bwd(ctypes.byref(plan.desc),
                                      _dev(g_recv, torch.bfloat16, "g_recv", D),
-                                     H, _dev(gx, torch.bfloat16, "gx", D), _stream(stream)))
+                                     H, _dev(gx, torch.bfloat16, "gx", D), _stream(stream, D)))
     return gx
 
 
@@ -263,7 +277,7 @@ def moonep_combine_bwd(plan: Plan, dout, y, g_y=None, dw=None, stream=None):
     _check(lib().moonep_combine_bwd(ctypes.byref(plan.desc), _dev(dout, torch.bfloat16, "dout", D),
                                     _dev(y, torch.bfloat16, "y", D), H,
                                     _dev(g_y, torch.bfloat16, "g_y", D),
-                                    _dev(dw, torch.float32, "dw", D), _stream(stream)))
+                                    _dev(dw, torch.float32, "dw", D), _stream(stream, D)))
     return g_y, dw
 
 
@@ -282,7 +296,7 @@ def moonep_prefetch_weight(plan: Plan, home_w, slot_w=None, stream=None):
     sp = _dev(slot_w, torch.bfloat16, "slot_w", D) if slot_w.numel() else ctypes.c_void_p(0)
     _check(lib().moonep_prefetch_weight(ctypes.byref(plan.desc),
                                         _dev(home_w, torch.bfloat16, "home_w", D), W_el, sp,
-                                        _stream(stream)))
+                                        _stream(stream, D)))
     return slot_w
 
 
@@ -306,7 +320,7 @@ def moonep_expert_stub(plan: Plan, topk_ids, recv, home_w, slot_w, y=None, strea
                                     _dev(topk_ids, torch.int32, "topk_ids", D),
                                     _dev(recv, torch.bfloat16, "recv", D),
                                     _dev(home_w, torch.bfloat16, "home_w", D), sp, W_el, H,
-                                    _dev(y, torch.bfloat16, "y", D), _stream(stream)))
+                                    _dev(y, torch.bfloat16, "y", D), _stream(stream, D)))
     return y
 
 
@@ -322,12 +336,13 @@ def moonep_reduce_grad(plan: Plan, home_grad, rep_grad, stream=None):
     rep_p = _dev(rep_grad, torch.float32, "rep_grad", D) if rep_grad.numel() else ctypes.c_void_p(0)
     _check(lib().moonep_reduce_grad(ctypes.byref(plan.desc),
                                     _dev(home_grad, torch.float32, "home_grad", D), rep_p, G_el,
-                                    _stream(stream)))
+                                    _stream(stream, D)))
     return home_grad
 
 
 def moonep_plan_status(plan: Plan, stream=None) -> dict:
     """Wait for the stream, then return the plan's statistics."""
     st = PlanStats()
-    _check(lib().moonep_plan_status(ctypes.byref(plan.desc), ctypes.byref(st), _stream(stream)))
+    _check(lib().moonep_plan_status(ctypes.byref(plan.desc), ctypes.byref(st),
+                                    _stream(stream, plan.blob.device)))
     return {n: getattr(st, n) for n, _ in PlanStats._fields_}

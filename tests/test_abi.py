@@ -1,6 +1,8 @@
-"""The C ABI library loads, exports every function include/moonep.h declares, and its
-host-only calls behave as documented.  No GPU work is launched here: moonep_query and the
-argument checks of the other calls run on the host."""
+"""The C ABI libraries load and export every function include/*.h declares
+(include/moonep.h: libmoonep.so, the hot path; include/moonep_streams.h:
+libmoonep_streams.so, the benchmark's memory streams), and their host-only calls behave
+as documented.  No GPU work is launched here: moonep_query and the argument checks of the
+other calls run on the host."""
 
 import ctypes
 import os
@@ -14,12 +16,13 @@ from oracle import moonep_oracle as O
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moonep.h")
+STREAMS_HEADER = os.path.join(ROOT, "include", "moonep_streams.h")
 
 EINVAL, ELIMIT, EPLAN, EHIP, EALIGN = -1, -2, -3, -4, -5
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(moonep_\w+)\s*\(", text)))
 
@@ -36,6 +39,29 @@ def test_every_declared_function_is_exported(lib):
     assert set(names) == set(M.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_headers_cover_every_library():
+    hdrs = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+    assert hdrs == ["moonep.h", "moonep_streams.h"], hdrs
+
+
+def test_streams_library_exports_its_header():
+    from combine_top_id_amd import streams
+    if not os.path.exists(streams.LIB_PATH):
+        pytest.fail("libmoonep_streams.so is not built (run __graft_entry__.build())")
+    L = streams.lib()
+    names = declared_functions(STREAMS_HEADER)
+    assert set(names) == set(streams.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+    # argument checks run on the host: nothing is launched
+    fake = ctypes.c_void_p(256)
+    assert L.moonep_stream_read(None, 4096, 1, 1, fake, None) == EINVAL
+    assert L.moonep_stream_write(fake, 4095, 1, 1, None) == EINVAL        # not 16-byte sized
+    assert L.moonep_stream_copy(fake, fake, 4096, 7, 1, None) == EINVAL    # unknown shape
+    assert L.moonep_rows_fanout(fake, 4, 0, fake, fake, 8, 64, 1, None) == EINVAL   # K < 1
+    assert L.moonep_rows_gather(fake, 4, 2, fake, 8, fake, 24, 1, None) == EINVAL   # row bytes
 
 
 @pytest.mark.parametrize("R,E,K,S,slots", [(4, 16, 2, 64, 4), (8, 64, 6, 1024, 8),

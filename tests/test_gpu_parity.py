@@ -4,7 +4,8 @@ Bar: plan arrays, dst_row, copied weights and dispatched rows bit-exact; combine
 rtol 1e-2 (bf16 output) and reduce within rtol 1e-5 (fp32), both also expected to be
 bit-exact because the kernels round each product and sum in the oracle's order.
 Small workloads are compared element by element; the full-size workloads compare every
-plan array and every dst_row, and dispatch/combine/reduce on sampled tokens and experts.
+plan array, every dst_row, every dispatched row (and that padding rows stay untouched),
+every combined token and every reduced expert.
 """
 
 import json
@@ -273,6 +274,15 @@ def test_bad_ids_give_empty_plan():
     assert (recv == 0).all()
     out = M.moonep_combine(plan, recv)
     assert (out == 0).all()
+    # the staged A/B path keeps the same contract: nothing mapped, zero output rows, even
+    # when the staging buffer holds NaN from earlier use
+    stage = torch.full((R * S * K, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    recv_s = torch.zeros_like(recv)
+    M.moonep_dispatch_staged(plan, x, recv_s, stage)
+    assert (recv_s == 0).all()
+    stage.fill_(float("nan"))
+    out_s = M.moonep_combine_staged(plan, recv, stage=stage)
+    assert (bf16_bits(out_s) == 0).all(), "staged combine of an invalid plan must write zero rows"
     home, rep = make_grads(E, R, slots, 16, 2, device="cuda")
     h0 = home.clone()
     M.moonep_reduce_grad(plan, home, rep)
@@ -297,6 +307,24 @@ def test_argument_errors():
     M.moonep_dispatch(plan, big[8:136].view(8, 16))       # 16-byte aligned: fine
     with pytest.raises(M.MoonepError):
         M.moonep_dispatch(plan, big[1:129].view(8, 16))   # 2-byte offset: EALIGN
+    # the staged wrappers check every tensor's size on the host: nothing is launched
+    H = 16
+    ok_x = torch.zeros(8, H, dtype=torch.bfloat16, device=dev)
+    ok_recv = torch.zeros(plan.sz.recv_rows, H, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(M.MoonepError):
+        M.moonep_dispatch_staged(plan, ok_x[:7], ok_recv)                 # x too small
+    with pytest.raises(M.MoonepError):
+        M.moonep_dispatch_staged(plan, ok_x, ok_recv[:-1])                # recv too small
+    with pytest.raises(M.MoonepError):
+        M.moonep_combine_staged(plan, ok_recv[:-1])                       # y too small
+    with pytest.raises(M.MoonepError):
+        M.moonep_combine_staged(plan, ok_recv, ok_x[:7])                  # out too small
+    with pytest.raises(M.MoonepError):
+        M.moonep_dispatch_staged(plan, ok_x, ok_recv, torch.zeros(1, H, dtype=torch.bfloat16,
+                                                                   device=dev))   # stage
+    # weights on another device than the ids: refused before any launch
+    with pytest.raises(M.MoonepError):
+        M.moonep_plan(ids, w.cpu(), 4, 16, 2, 2, 4)
     torch.cuda.synchronize()
 
 
@@ -318,7 +346,8 @@ def test_plan_is_deterministic_and_reusable():
 
 
 # ----------------------------------------------------------------------------------------
-# full-size workloads: whole plan and dst_row; sampled data movement
+# full-size workloads: whole plan, dst_row, every dispatched row, padding, every combined
+# token and every reduced expert
 # ----------------------------------------------------------------------------------------
 
 BIG = [(DSV3, i) for i in range(4)] + [(KIMI, 0)] + [(DECODE, i) for i in range(2)]
@@ -338,7 +367,9 @@ def test_full_size(wl, mi):
     assert_plan_matches(got, p, dst)
 
     x = make_hidden(wl.T, wl.H, seed + 1, device="cuda")
-    recv = M.moonep_dispatch(plan, x)
+    nan_bits = int(bf16_bits(torch.tensor([float("nan")], dtype=torch.bfloat16))[0])
+    recv = torch.full((plan.sz.recv_rows, wl.H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    M.moonep_dispatch(plan, x, recv)
     rng = np.random.default_rng(seed)
     tok = np.unique(np.concatenate([rng.choice(wl.T, 384, replace=False), [0, wl.T - 1]]))
     x_s = bf16_bits(x[torch.from_numpy(tok).cuda()])
@@ -352,37 +383,52 @@ def test_full_size(wl, mi):
         c1 = min(c0 + 4096, wl.T)
         g = recv[all_rows[c0 * wl.K:c1 * wl.K]].view(c1 - c0, wl.K, wl.H)
         assert torch.equal(g, x[c0:c1, None, :].expand(-1, wl.K, -1))
-    del recv
+    # padding rows (no assignment maps there) are never written
+    pad = torch.ones(plan.sz.recv_rows, dtype=torch.bool, device="cuda")
+    pad[all_rows] = False
+    pad_rows = recv[pad].view(torch.int16)
+    assert pad_rows.shape[0] == plan.sz.recv_rows - wl.A
+    assert bool((pad_rows == np.int16(np.uint16(nan_bits).view(np.int16))).all()), \
+        "padding rows must not be written"
+    del recv, pad, pad_rows
 
-    # combine on an independent expert output y (seeded), sampled tokens vs the oracle
+    # combine on an independent expert output y (seeded): every token against the oracle,
+    # in chunks of tokens (rows gathered on the GPU, the oracle run on the host)
     y = make_hidden(plan.sz.recv_rows, wl.H, seed + 2, device="cuda")
     out = M.moonep_combine(plan, y)
-    y_rows = bf16_bits(y[r_t]).reshape(len(tok) * wl.K, wl.H)
-    local_dst = np.arange(len(tok) * wl.K).reshape(len(tok), wl.K)
-    ref = O.combine(local_dst, w_np[tok], y_rows)
-    got_out = bf16_bits(out[torch.from_numpy(tok).cuda()])
-    assert_close(O.bf16_to_f32(got_out), O.bf16_to_f32(ref), RTOL_BF16)
-    assert (got_out == ref).all()
+    ch = 2048
+    local_dst = np.arange(ch * wl.K).reshape(ch, wl.K)
+    for c0 in range(0, wl.T, ch):
+        c1 = min(c0 + ch, wl.T)
+        y_rows = bf16_bits(y[all_rows[c0 * wl.K:c1 * wl.K]])
+        ref = O.combine(local_dst[:c1 - c0], w_np[c0:c1], y_rows)
+        got_out = bf16_bits(out[c0:c1])
+        assert_close(O.bf16_to_f32(got_out), O.bf16_to_f32(ref), RTOL_BF16)
+        assert (got_out == ref).all(), f"combine tokens {c0}..{c1}"
     del y, out
 
     if wl.G_el:
+        # every expert of the reduce list against home + its slot replicas in piece order;
+        # every other expert untouched
         home, rep = make_grads(wl.E, wl.R, wl.slots, wl.G_el, seed + 3, device="cuda")
-        others = torch.tensor([e for e in range(wl.E) if e not in set(got["red"].tolist())][:4],
-                              device="cuda")
-        o_before = home[others].clone()
-        red = got["red"][:6]
-        h_before = home[torch.from_numpy(red.astype(np.int64)).cuda()].cpu().numpy()
-        pieces = [tuple(q) for q in p.pieces if q[0] in set(red.tolist())]
-        need = sorted({(int(q[1]), int(q[2])) for q in pieces if q[2] >= 0})
+        red = got["red"]
+        assert len(red) == len({int(q[0]) for q in p.pieces if q[2] >= 0})
+        is_red = torch.zeros(wl.E, dtype=torch.bool, device="cuda")
+        is_red[torch.from_numpy(red.astype(np.int64)).cuda()] = True
+        o_before = home[~is_red].clone()
+        h_before = home[is_red].cpu().numpy()           # experts in id order
+        red_ids = np.flatnonzero(is_red.cpu().numpy())
+        need = sorted({(int(q[1]), int(q[2])) for q in p.pieces if q[2] >= 0})
         rep_s = {k: rep[k[0], k[1]].cpu().numpy() for k in need}
         M.moonep_reduce_grad(plan, home, rep)
-        h_after = home[torch.from_numpy(red.astype(np.int64)).cuda()].cpu().numpy()
-        for n, e in enumerate(red):
+        h_after = home[is_red].cpu().numpy()
+        for n, e in enumerate(red_ids):
             ref_e = h_before[n].copy()
             for (pe, r, slot, cnt, start, fb) in p.pieces:
                 if pe == e and slot >= 0:
                     ref_e = (ref_e + rep_s[(int(r), int(slot))]).astype(np.float32)
-            assert (h_after[n].view(np.uint32) == ref_e.view(np.uint32)).all()
-        assert torch.equal(home[others], o_before)     # experts without replicas untouched
-        del home, rep
+            assert_close(h_after[n], ref_e, RTOL_FP32)
+            assert (h_after[n].view(np.uint32) == ref_e.view(np.uint32)).all(), f"reduce expert {e}"
+        assert torch.equal(home[~is_red], o_before)     # experts without replicas untouched
+        del home, rep, o_before
     torch.cuda.synchronize()
