@@ -1,5 +1,6 @@
 // The C ABI: argument checks, sizes, and the launches on the caller's stream.
 #include <cstring>
+#include <mutex>
 
 #include "moonep_internal.h"
 
@@ -22,6 +23,32 @@ int check_desc(const moonep_plan_desc* d) {
 // call caused it.  Each entry point clears it right before its launches, so the status it
 // reads afterwards belongs to its own launches only.
 void clear_error() { (void)hipGetLastError(); }
+
+// The planning workspace of moonep_plan_noalloc: a file-scope device array, one copy per
+// GPU the library runs on, held until the process ends.  Host code never uses the name
+// `scratch` as an address (on the host it is only a stand-in for the symbol); each
+// device's own address comes from hipGetSymbolAddress, looked up once per device with that
+// device current, and is what the kernels receive.  Nothing in the planning kernels needs
+// the workspace to start at zero: every word they read was written earlier in the same
+// plan.
+constexpr int64_t kNoAllocWorkspaceBytes = MOONEP_NOALLOC_WORKSPACE_MAX;
+__device__ __align__(256) int32_t scratch[kNoAllocWorkspaceBytes / 4];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (nullptr on a HIP error).
+void* device_scratch(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
 
 }  // namespace
 
@@ -54,6 +81,30 @@ int moonep_plan(const int32_t* topk_ids, const float* topk_w, int R, int E, int 
   clear_error();
   const hipError_t err = launch_plan(s, topk_ids, topk_w, static_cast<int32_t*>(plan_dev),
                                      static_cast<int32_t*>(workspace), stream);
+  return err == hipSuccess ? MOONEP_OK : MOONEP_EHIP;
+}
+
+int moonep_plan_noalloc(const int32_t* topk_ids, const float* topk_w, int R, int E, int K, int S,
+                        int slots, void* plan_dev, moonep_plan_desc* desc, hipStream_t stream) {
+  if (!topk_ids || !topk_w || !plan_dev || !desc) return MOONEP_EINVAL;
+  moonep_sizes s;
+  std::memset(&s, 0, sizeof(s));
+  const int rc = fill_sizes(R, E, K, S, slots, &s);
+  if (rc != MOONEP_OK) return rc;
+  if (s.workspace_bytes > kNoAllocWorkspaceBytes) return MOONEP_ELIMIT;
+  if (!aligned(plan_dev, 256) || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return MOONEP_EALIGN;
+  int dev = -1, sdev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || hipStreamGetDevice(stream, &sdev) != hipSuccess)
+    return MOONEP_EHIP;
+  if (sdev != dev) return MOONEP_EINVAL;      // the stream must belong to the current device
+  void* ws = device_scratch(dev);
+  if (!ws) return MOONEP_EHIP;
+  desc->magic = kMagic;
+  desc->sz = s;
+  desc->dev = plan_dev;
+  clear_error();
+  const hipError_t err = launch_plan(s, topk_ids, topk_w, static_cast<int32_t*>(plan_dev),
+                                     static_cast<int32_t*>(ws), stream);
   return err == hipSuccess ? MOONEP_OK : MOONEP_EHIP;
 }
 

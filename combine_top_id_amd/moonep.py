@@ -57,6 +57,8 @@ def lib():
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     L.moonep_query.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(Sizes)]
     L.moonep_plan.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, ctypes.POINTER(PlanDesc), vp]
+    L.moonep_plan_noalloc.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, ctypes.POINTER(PlanDesc),
+                                      vp]
     L.moonep_dispatch.argtypes = [ctypes.POINTER(PlanDesc), vp, i32, vp, vp]
     L.moonep_combine.argtypes = [ctypes.POINTER(PlanDesc), vp, i32, vp, vp]
     L.moonep_reduce_grad.argtypes = [ctypes.POINTER(PlanDesc), vp, vp, i64, vp]
@@ -69,7 +71,7 @@ def lib():
     L.moonep_plan_status.argtypes = [ctypes.POINTER(PlanDesc), ctypes.POINTER(PlanStats), vp]
     L.moonep_strerror.argtypes = [i32]
     L.moonep_strerror.restype = ctypes.c_char_p
-    for f in ("moonep_query", "moonep_plan", "moonep_dispatch",
+    for f in ("moonep_query", "moonep_plan", "moonep_plan_noalloc", "moonep_dispatch",
               "moonep_combine",
               "moonep_reduce_grad", "moonep_plan_status", "moonep_dispatch_bwd",
               "moonep_combine_bwd", "moonep_prefetch_weight", "moonep_expert_stub",
@@ -79,7 +81,7 @@ def lib():
     return L
 
 
-EXPORTS = ("moonep_query", "moonep_plan", "moonep_dispatch",
+EXPORTS = ("moonep_query", "moonep_plan", "moonep_plan_noalloc", "moonep_dispatch",
            "moonep_combine",
            "moonep_reduce_grad", "moonep_plan_status", "moonep_strerror",
            "moonep_dispatch_bwd", "moonep_combine_bwd", "moonep_prefetch_weight",
@@ -161,7 +163,7 @@ def moonep_plan(topk_ids, topk_w, R, E, K, S, slots, plan=None, stream=None) -> 
     w_p = _dev(topk_w, torch.float32, "topk_w", topk_ids.device)
     if topk_ids.numel() != sz.A or topk_w.numel() != sz.A:
         raise MoonepError("topk_ids / topk_w must hold R*S*K elements")
-    if plan is None or plan.sz.plan_bytes != sz.plan_bytes or \
+    if plan is None or plan.workspace is None or plan.sz.plan_bytes != sz.plan_bytes or \
             plan.sz.workspace_bytes != sz.workspace_bytes:
         plan = Plan(sz, _blob(sz.plan_bytes, topk_ids.device),
                     _blob(sz.workspace_bytes, topk_ids.device))
@@ -170,6 +172,26 @@ def moonep_plan(topk_ids, topk_w, R, E, K, S, slots, plan=None, stream=None) -> 
                              ctypes.c_void_p(plan.blob.data_ptr()),
                              ctypes.c_void_p(plan.workspace.data_ptr()),
                              ctypes.byref(plan.desc), _stream(stream, topk_ids.device)))
+    return plan
+
+
+def moonep_plan_noalloc(topk_ids, topk_w, R, E, K, S, slots, plan=None, stream=None) -> Plan:
+    """moonep_plan through the entry point that allocates nothing: the planning workspace is
+    the library's static per-GPU array (at most MOONEP_NOALLOC_WORKSPACE_MAX bytes).  The
+    plan blob is the caller's (`plan`'s, else one allocated here, outside the C call)."""
+    sz = moonep_query(R, E, K, S, slots)
+    D = topk_ids.device
+    ids_p = _dev(topk_ids, torch.int32, "topk_ids")
+    w_p = _dev(topk_w, torch.float32, "topk_w", D)
+    if topk_ids.numel() != sz.A or topk_w.numel() != sz.A:
+        raise MoonepError("topk_ids / topk_w must hold R*S*K elements")
+    if plan is None or plan.sz.plan_bytes != sz.plan_bytes or plan.blob.device != D:
+        plan = Plan(sz, _blob(sz.plan_bytes, D), None)
+    plan.sz = sz
+    with torch.cuda.device(D):       # the library uses the current device's array
+        _check(lib().moonep_plan_noalloc(ids_p, w_p, R, E, K, S, slots,
+                                         ctypes.c_void_p(plan.blob.data_ptr()),
+                                         ctypes.byref(plan.desc), _stream(stream, D)))
     return plan
 
 

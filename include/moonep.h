@@ -20,14 +20,16 @@
  * Conventions for every call:
  *   - Device pointers are plain HIP device addresses; the caller owns and allocates all
  *     memory.  The library never allocates, frees or synchronises (except
- *     moonep_plan_status, which waits on `stream`).
+ *     moonep_plan_status, which waits on `stream`).  moonep_plan_noalloc alone uses
+ *     library-owned device memory: a static per-GPU workspace array.
  *   - All GPU work is enqueued on `stream` (0 = the null stream) and is asynchronous.
  *   - Return value: MOONEP_OK (0) or a negative MOONEP_E* code.  On an error return
  *     nothing was enqueued.  Data errors found on the device (an expert id outside
  *     [0, E)) are never reported by a return code: they set the plan's status word,
  *     read with moonep_plan_status; such a plan maps nothing (every dst_row is -1),
  *     dispatch then writes nothing, combine writes zero rows and reduce adds nothing.
- *   - Calls are thread-safe; the library has no global mutable state.
+ *   - Calls are thread-safe; the library has no global mutable state apart from
+ *     moonep_plan_noalloc's per-GPU workspace array (see there).
  */
 #ifndef MOONEP_H_
 #define MOONEP_H_
@@ -44,6 +46,8 @@ extern "C" {
 #define MOONEP_MAX_E 1024
 #define MOONEP_MAX_K 32
 #define MOONEP_MAX_SLOTS 256
+/* largest planning workspace moonep_plan_noalloc serves from its static device array */
+#define MOONEP_NOALLOC_WORKSPACE_MAX (8 << 20)
 
 enum {
   MOONEP_OK = 0,
@@ -116,6 +120,23 @@ int moonep_query(int R, int E, int K, int S, int slots, moonep_sizes* out);
 int moonep_plan(const int32_t* topk_ids, const float* topk_w, int R, int E, int K, int S,
                 int slots, void* plan_dev, void* workspace, moonep_plan_desc* desc,
                 hipStream_t stream);
+
+/* moonep_plan for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments, result
+ * and errors as moonep_plan, without `workspace`: the planning kernels use a file-scope
+ * device array of MOONEP_NOALLOC_WORKSPACE_MAX bytes (8 MiB; enough for every
+ * (R, E, K, S, slots) whose moonep_sizes.workspace_bytes is at most that), one copy per GPU,
+ * held until the process ends.  The call allocates and frees nothing; the caller still
+ * provides topk_ids, topk_w and the plan blob.
+ *   ELIMIT  when workspace_bytes exceeds MOONEP_NOALLOC_WORKSPACE_MAX (nothing enqueued)
+ *   EINVAL  when `stream` does not belong to the current device (the array used is the
+ *           current device's)
+ * Every call on one GPU shares that GPU's array: two of these calls whose kernels overlap
+ * in time on the same GPU (different streams, or different host threads without ordering)
+ * race and may both produce wrong plans.  Calls ordered on one stream are safe.  The array
+ * need not start at zero and keeps the last call's contents. */
+int moonep_plan_noalloc(const int32_t* topk_ids, const float* topk_w, int R, int E, int K, int S,
+                        int slots, void* plan_dev, moonep_plan_desc* desc, hipStream_t stream);
 
 /* Zero-copy dispatch ("MoonshotAI/MoonEP 딥다이브", section 2, point 2: each token row
  * is written straight into its final expert position; no permute, no staging copy):

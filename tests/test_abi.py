@@ -105,6 +105,14 @@ def test_calls_reject_bad_arguments_on_the_host(lib):
     assert lib.moonep_plan(fake, fake, 3, 16, 2, 4, 4, fake, fake, ctypes.byref(d), None) == EINVAL
     assert lib.moonep_plan(fake, fake, 4, 16, 2, 4, 4, ctypes.c_void_p(260), fake,
                            ctypes.byref(d), None) == EALIGN
+    # the no-allocation variant: the same host checks, and a workspace beyond its static
+    # array is refused before any HIP call
+    assert lib.moonep_plan_noalloc(None, fake, 4, 16, 2, 4, 4, fake, ctypes.byref(d), None) == EINVAL
+    assert lib.moonep_plan_noalloc(fake, fake, 3, 16, 2, 4, 4, fake, ctypes.byref(d), None) == EINVAL
+    big = M.moonep_query(64, 1024, 32, 1 << 13, 8)
+    assert big.workspace_bytes > (8 << 20)
+    assert lib.moonep_plan_noalloc(fake, fake, 64, 1024, 32, 1 << 13, 8, fake, ctypes.byref(d),
+                                   None) == ELIMIT
     # an uninitialised descriptor is refused by every call that takes one
     assert lib.moonep_dispatch(ctypes.byref(d), fake, 16, fake, None) == EPLAN
     assert lib.moonep_combine(ctypes.byref(d), fake, 16, fake, None) == EPLAN
