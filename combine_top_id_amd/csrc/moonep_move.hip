@@ -65,6 +65,22 @@ constexpr int kDispU = 2;
 constexpr int kDispChunk = kWave * kDispU;     // 128 vectors = 2 KB of a bf16 row
 constexpr int kCombChunk = kWave;              // 64 vectors = 1 KB of a bf16 row
 
+// Residency caps.  Each launch requests dynamic LDS that the kernels never touch, so that
+// at most floor(160 KB / request) of their single-wave workgroups sit on a CU at once
+// (gfx950: 160 KB of LDS per CU): fewer tokens in flight, fewer rows of the big buffer
+// open at once.  Measured on MI355X with the product kernels (interleaved A/B, one
+// process; sweep of 14-29 KB per workgroup):
+//   dispatch, 6 per CU: DeepSeek-V3-shaped routing +4-8% over no cap at every maxvio,
+//     decode +3%, the 8-rank/64-expert workload +7%, Kimi scale unchanged (its own best,
+//     7 per CU, is +5% there but gains nothing at DeepSeek-V3 shape);
+//   combine, 8 per CU: +1.5-8% while the gathered rows are far larger than the 256 MB
+//     last-level cache, but -7% when they fit in it (more rows in flight then win), so
+//     the cap applies only to buffers larger than that cache.
+// Each request sits mid-interval, clear of the LDS allocation granularity.
+constexpr int kDispLdsBytes = 25 * 1024;       // 6 dispatch workgroups per CU
+constexpr int kCombLdsBytes = 19 * 1024;       // 8 combine workgroups per CU
+constexpr int64_t kLastLevelCacheBytes = 256ll << 20;   // MI355X Infinity Cache
+
 template <int KT, bool STAGED>
 __global__ __launch_bounds__(kWave) void dispatch_kernel(const int32_t* __restrict__ dst,
                                                          const u32x4* __restrict__ x,
@@ -477,7 +493,8 @@ __global__ __launch_bounds__(kRedThreads) void reduce_kernel(const int32_t* __re
 template <int KT, bool STAGED>
 void launch_dispatch_k(const moonep_sizes& s, const int32_t* dst, int nrows, const uint16_t* x,
                        uint16_t* recv, int nvec, int nch, hipStream_t st) {
-  hipLaunchKernelGGL((dispatch_kernel<KT, STAGED>), dim3((unsigned)(s.T * nch)), dim3(kWave), 0, st,
+  hipLaunchKernelGGL((dispatch_kernel<KT, STAGED>), dim3((unsigned)(s.T * nch)), dim3(kWave),
+                     kDispLdsBytes, st,
                      dst, reinterpret_cast<const u32x4*>(x), reinterpret_cast<u32x4*>(recv), s.K, nvec,
                      nch, nrows);
 }
@@ -500,8 +517,11 @@ void dispatch_rows(const moonep_sizes& s, const int32_t* dst, int nrows, const u
 template <int KT, bool WEIGHTED, bool STAGED>
 void launch_combine_k(const moonep_sizes& s, const int32_t* dst, const float* w, const uint16_t* y,
                       uint16_t* out, int nvec, int nch, hipStream_t st) {
+  // the rows gathered: the receive-shaped buffer, or the [T*K, H] staging buffer
+  const int64_t src_bytes = (STAGED ? s.A : s.recv_rows) * (int64_t)nvec * 16;
+  const int lds = src_bytes > kLastLevelCacheBytes ? kCombLdsBytes : 0;
   hipLaunchKernelGGL((combine_kernel<KT, WEIGHTED, STAGED>), dim3((unsigned)(s.T * nch)), dim3(kWave),
-                     0, st, dst, w, reinterpret_cast<const u32x4*>(y), reinterpret_cast<u32x4*>(out),
+                     lds, st, dst, w, reinterpret_cast<const u32x4*>(y), reinterpret_cast<u32x4*>(out),
                      s.K, nvec, nch, (int)s.recv_rows);
 }
 
