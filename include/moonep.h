@@ -23,8 +23,11 @@
  *     moonep_plan_status, which waits on `stream`).  moonep_plan_noalloc alone uses
  *     library-owned device memory: a static per-GPU workspace array.
  *   - All GPU work is enqueued on `stream` (0 = the null stream) and is asynchronous.
- *   - Return value: MOONEP_OK (0) or a negative MOONEP_E* code.  On an error return
- *     nothing was enqueued.  Data errors found on the device (an expert id outside
+ *   - Return value: MOONEP_OK (0) or a negative MOONEP_E* code.  Argument errors
+ *     (EINVAL, ELIMIT, EALIGN, EPLAN) are found on the host and nothing is enqueued; an
+ *     EHIP from a call that launches several kernels (moonep_plan, the staged calls) can
+ *     follow launches of that call that were already enqueued.  Each call clears the
+ *     thread's earlier HIP error before launching, so an EHIP is its own.  Data errors found on the device (an expert id outside
  *     [0, E)) are never reported by a return code: they set the plan's status word,
  *     read with moonep_plan_status; such a plan maps nothing (every dst_row is -1),
  *     dispatch then writes nothing, combine writes zero rows and reduce adds nothing.
@@ -93,8 +96,12 @@ typedef struct moonep_plan_stats {
   int32_t max_load;         /* largest per-expert load                                   */
 } moonep_plan_stats;
 
-/* Sizes for a problem, host only.  EINVAL unless R>=1, E%R==0, 1<=K<=E, S>=1, slots>=0;
- * ELIMIT beyond R<=64, E<=1024, K<=32, slots<=256, or when R*NvS or T*K exceeds int32. */
+/* Sizes for a problem, host only ("MoonshotAI/MoonEP 딥다이브", section 4, design
+ * pattern 2: per-rank buffers have a static size, S*K rows plus alignment padding, fixed
+ * before any routing is seen; section 2, point 3: so the host never waits for the device
+ * to learn how much to allocate).  Every buffer the other calls take is sized from here.
+ * EINVAL unless R>=1, E%R==0, 1<=K<=E, S>=1, slots>=0; ELIMIT beyond R<=64, E<=1024,
+ * K<=32, slots<=256, or when R*NvS or T*K exceeds int32. */
 int moonep_query(int R, int E, int K, int S, int slots, moonep_sizes* out);
 
 /* Planning ("Moonshot AI Open-Sources MoonEP", paragraph 3: duplicate a few overloaded
@@ -107,6 +114,17 @@ int moonep_query(int R, int E, int K, int S, int slots, moonep_sizes* out);
  *   workspace  device scratch of moonep_sizes.workspace_bytes, 256-byte aligned; free
  *              for reuse once the plan's kernels have run on `stream`
  *   desc       host handle, filled synchronously (sizes + plan_dev)
+ *
+ * Boundary note.  The plan is a device blob, as in a blob-only signature, but the call also
+ * fills `desc`, a host copy of the problem's sizes plus the blob's address, and every
+ * later call takes `desc` instead of the bare blob.  The sizes of every launch (grid,
+ * rows, K) are then known on the host without reading the device, so no call ever waits
+ * for the plan (the deep dive's section 2, point 3: no per-layer host synchronisation);
+ * the blob itself stays on the device and is what the kernels read.
+ *
+ * Errors: EINVAL, ELIMIT and EALIGN are found on the host before anything is enqueued;
+ * EHIP means a launch failed, in which case kernels launched before it by this call may
+ * already be enqueued (the plan is then unusable until a later call succeeds).
  *
  * The plan rule: experts are taken by (load descending, id ascending); an expert on a
  * home whose load exceeds S*K sheds min(load, remaining excess); each shed assignment
@@ -231,7 +249,11 @@ int moonep_expert_stub(const moonep_plan_desc* plan, const int32_t* topk_ids,
                        int64_t W_el, int H, uint16_t* y, hipStream_t stream);
 
 /* Waits for `stream`, then copies the plan's statistics to the host.  The only call
- * that synchronises. */
+ * that synchronises: the hot path itself never reads the plan back ("MoonshotAI/MoonEP
+ * 딥다이브", section 2, point 3: static buffers remove the per-layer host sync), so data
+ * errors found on the device (status 1: an expert id outside [0, E); status 2: an
+ * internal invariant of the plan failed) are reported here, when the caller asks, and
+ * meanwhile make the plan map nothing. */
 int moonep_plan_status(const moonep_plan_desc* plan, moonep_plan_stats* out,
                        hipStream_t stream);
 
