@@ -358,6 +358,19 @@ def main():
             row.update(reduce_us=round(tr, 2), reduce_gbps=round(rb / tr / 1e3, 1))
         rows.append(row)
 
+    # plan latency back to back: 20 plans of the first batch between one event pair (the
+    # event-bracketed figures above include the launch latency after each event)
+    pe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    b0 = batches[0]
+    for _ in range(3):
+        plan = M.moonep_plan(b0["ids"], b0["w"], wl.R, wl.E, wl.K, wl.S, wl.slots, plan=plan)
+    pe[0].record(stream)
+    for _ in range(20):
+        plan = M.moonep_plan(b0["ids"], b0["w"], wl.R, wl.E, wl.K, wl.S, wl.slots, plan=plan)
+    pe[1].record(stream)
+    torch.cuda.synchronize()
+    plan_b2b_us = pe[0].elapsed_time(pe[1]) * 1e3 / 20
+
     all_d = [v for d in per for v in d["disp"]]
     all_c = [v for d in per for v in d["comb"]]
     mean_d, mean_c = statistics.mean(all_d), statistics.mean(all_c)
@@ -508,6 +521,7 @@ def main():
         "per_maxvio": rows,
         "flatness_max_over_min": round(max(dc_times) / min(dc_times), 4),
         "plan_us_median": round(statistics.median([r["plan_us"] for r in rows]), 2),
+        "plan_us_back_to_back": round(plan_b2b_us, 2),
         "ceilings": ceil,
         "backward": backward,
         "prefetch": prefetch,

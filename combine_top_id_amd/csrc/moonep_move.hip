@@ -68,17 +68,19 @@ constexpr int kCombChunk = kWave;              // 64 vectors = 1 KB of a bf16 ro
 // Residency caps.  Each launch requests dynamic LDS that the kernels never touch, so that
 // at most floor(160 KB / request) of their single-wave workgroups sit on a CU at once
 // (gfx950: 160 KB of LDS per CU): fewer tokens in flight, fewer rows of the big buffer
-// open at once.  Measured on MI355X with the product kernels (interleaved A/B, one
-// process; sweep of 14-29 KB per workgroup):
-//   dispatch, 6 per CU: DeepSeek-V3-shaped routing +4-8% over no cap at every maxvio,
-//     decode +3%, the 8-rank/64-expert workload +7%, Kimi scale unchanged (its own best,
-//     7 per CU, is +5% there but gains nothing at DeepSeek-V3 shape);
-//   combine, 8 per CU: +1.5-8% while the gathered rows are far larger than the 256 MB
-//     last-level cache, but -7% when they fit in it (more rows in flight then win), so
-//     the cap applies only to buffers larger than that cache.
+// open at once.  Chosen on MI355X inside the real step (plan -> dispatch -> combine,
+// cycling through the routing batches, interleaved variants of the library in one
+// process), which is where it counts: the cache and memory state the previous kernel
+// leaves behind moves the optimum against back-to-back launches of one kernel.
+//   combine, 9 per CU: +8% over no cap at DeepSeek-V3 shape, +11% at Kimi scale, and
+//     7, 8, 10 or 11 per CU all lose to 9 there and at decode; but -7% when the gathered rows
+//     fit in the 256 MB last-level cache (more rows in flight then win), so the cap
+//     applies only to larger buffers;
+//   dispatch, 6 per CU: +0.3% at DeepSeek-V3 shape and Kimi scale, +1.7% at decode
+//     (Kimi's own best, 7 per CU, is +3% there and -1.7% at DeepSeek-V3 shape).
 // Each request sits mid-interval, clear of the LDS allocation granularity.
 constexpr int kDispLdsBytes = 25 * 1024;       // 6 dispatch workgroups per CU
-constexpr int kCombLdsBytes = 19 * 1024;       // 8 combine workgroups per CU
+constexpr int kCombLdsBytes = 17 * 1024;       // 9 combine workgroups per CU
 constexpr int64_t kLastLevelCacheBytes = 256ll << 20;   // MI355X Infinity Cache
 
 template <int KT, bool STAGED>
