@@ -56,6 +56,16 @@ void row_shape(int nvec, int umax, int upref, int* threads, int* u) {
 // A workgroup of one wave starts as soon as any wave slot of a CU frees, so the CUs stay
 // full of short-lived waves; larger workgroups wait for several free slots at once.
 //
+// One explicit wait separates the loads from the stores.  gfx9 counts stores in the
+// same vmcnt counter as loads, and the loads and stores here sit under conditions (a
+// partial last chunk, an unmapped row), so without it the compiler cannot tell how many
+// operations follow a load on a given path and places a vmcnt(0) before every store:
+// each of the K*kDispU stores of a wave then waits for the previous one's write
+// acknowledgement.  With the single wait the stores issue back to back: +2-3% at
+// DeepSeek-V3 shape and Kimi scale in the step at the same residency cap, and the best
+// cap moved from 6 to 5 workgroups per CU.  Waiting per vector instead (branch-free code
+// lets the compiler count exactly) measured 6% slower than waiting once for both.
+//
 // KT = K when K is a compile-time constant (the rows are then held in registers), else 0.
 // STAGED: the destination is row t*K + k of a [T*K, H] staging buffer (the non-zero-copy
 // A/B baseline), not the plan's row; it has its own instantiation so that profiles keep
@@ -64,6 +74,8 @@ constexpr int kWave = 64;
 constexpr int kDispU = 2;
 constexpr int kDispChunk = kWave * kDispU;     // 128 vectors = 2 KB of a bf16 row
 constexpr int kCombChunk = kWave;              // 64 vectors = 1 KB of a bf16 row
+// s_waitcnt vmcnt(0) in the gfx9 encoding, with expcnt and lgkmcnt left at their maximum
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 // Residency caps.  Each launch requests dynamic LDS that the kernels never touch, so that
 // at most floor(160 KB / request) of their single-wave workgroups sit on a CU at once
@@ -76,10 +88,11 @@ constexpr int kCombChunk = kWave;              // 64 vectors = 1 KB of a bf16 ro
 //     7, 8, 10 or 11 per CU all lose to 9 there and at decode; but -7% when the gathered rows
 //     fit in the 256 MB last-level cache (more rows in flight then win), so the cap
 //     applies only to larger buffers;
-//   dispatch, 6 per CU: +0.3% at DeepSeek-V3 shape and Kimi scale, +1.7% at decode
-//     (Kimi's own best, 7 per CU, is +3% there and -1.7% at DeepSeek-V3 shape).
+//   dispatch, 5 per CU: at DeepSeek-V3 shape and Kimi scale +2-4% over 6 per CU, +6-7%
+//     over 7 per CU and +3-9% over 4 per CU; within 1% of them at decode; with no cap
+//     the kernel loses 11%.
 // Each request sits mid-interval, clear of the LDS allocation granularity.
-constexpr int kDispLdsBytes = 25 * 1024;       // 6 dispatch workgroups per CU
+constexpr int kDispLdsBytes = 29 * 1024;       // 5 dispatch workgroups per CU
 constexpr int kCombLdsBytes = 17 * 1024;       // 9 combine workgroups per CU
 constexpr int64_t kLastLevelCacheBytes = 256ll << 20;   // MI355X Infinity Cache
 
@@ -94,15 +107,16 @@ __global__ __launch_bounds__(kWave) void dispatch_kernel(const int32_t* __restri
   const int32_t* d = STAGED ? nullptr : dst + t * K;
   const u32x4* src = x + t * nvec;
   u32x4 buf[kDispU];
-#pragma unroll
-  for (int u = 0; u < kDispU; ++u) {
-    const int v = c0 + u * kWave;
-    if (v < nvec) buf[u] = src[v];
-  }
   if constexpr (KT > 0) {
     int rows[KT];
 #pragma unroll
     for (int k = 0; k < KT; ++k) rows[k] = STAGED ? (int)(t * K + k) : d[k];
+#pragma unroll
+    for (int u = 0; u < kDispU; ++u) {
+      const int v = c0 + u * kWave;
+      if (v < nvec) buf[u] = src[v];
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 #pragma unroll
     for (int u = 0; u < kDispU; ++u) {
       const int v = c0 + u * kWave;
@@ -114,6 +128,12 @@ __global__ __launch_bounds__(kWave) void dispatch_kernel(const int32_t* __restri
       }
     }
   } else {
+#pragma unroll
+    for (int u = 0; u < kDispU; ++u) {
+      const int v = c0 + u * kWave;
+      if (v < nvec) buf[u] = src[v];
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     for (int k = 0; k < K; ++k) {
       const int row = STAGED ? (int)(t * K + k) : d[k];
       if ((unsigned)row >= (unsigned)nrows) continue;   // -1: unmapped

@@ -11,6 +11,17 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kEInval = -1, kEHip = -4;
 
+// s_waitcnt vmcnt(0) in the gfx9 encoding, with expcnt and lgkmcnt left at their maximum
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// The row streams use the hot path kernels' residency caps (dynamic LDS they never touch,
+// so that at most floor(160 KB / request) single-wave workgroups sit on a CU): 5 per CU
+// for the fan-out, 9 per CU for the gather when its source exceeds the 256 MB last-level
+// cache.
+constexpr int kFanoutLdsBytes = 29 * 1024;
+constexpr int kGatherLdsBytes = 17 * 1024;
+constexpr int64_t kLastLevelCacheBytes = 256ll << 20;
+
 template <int POL>
 __device__ __forceinline__ u32x4 load16(const u32x4* p) {
   if constexpr (POL == 1) return __builtin_nontemporal_load(p); else return *p;
@@ -68,7 +79,10 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src
   }
 }
 
-// dispatch's mix: one wave per (source row, 128-vector chunk)
+// dispatch's mix: one wave per (source row, 128-vector chunk), the dispatch kernel's
+// shape: the row indices and the two loads first, one wait for the loads (without it the
+// compiler waits for every earlier store before each store: vmcnt counts both), then the
+// stores back to back
 __global__ __launch_bounds__(64) void fanout_kernel(const int32_t* __restrict__ rows,
                                                     const u32x4* __restrict__ src,
                                                     u32x4* __restrict__ dst, int K, int nvec,
@@ -82,13 +96,18 @@ __global__ __launch_bounds__(64) void fanout_kernel(const int32_t* __restrict__ 
     if (v < nvec)
       b[u] = read_src ? src[i * nvec + v] : u32x4{(unsigned)i, (unsigned)v, 0x77777777u, 1u};
   }
-  for (int k = 0; k < K; ++k) {
-    const int64_t r = rows[i * K + k];
-    if (r < 0 || r >= dst_rows) continue;
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  for (int k0 = 0; k0 < K; k0 += 8) {
+    int64_t r[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = k0 + j < K ? rows[i * K + k0 + j] : -1;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int v = c0 + u * 64;
-      if (v < nvec) __builtin_nontemporal_store(b[u], dst + r * nvec + v);
+      if (v >= nvec) continue;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (r[j] >= 0 && r[j] < dst_rows) __builtin_nontemporal_store(b[u], dst + r[j] * nvec + v);
     }
   }
 }
@@ -208,8 +227,8 @@ int moonep_rows_fanout(const int32_t* rows, int64_t n, int K, const void* src, v
   const int nch = (nvec + 127) / 128;
   if (n * nch > INT32_MAX) return kEInval;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(fanout_kernel, dim3((unsigned)(n * nch)), dim3(64), 0, stream, rows,
-                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), K, nvec, nch,
+  hipLaunchKernelGGL(fanout_kernel, dim3((unsigned)(n * nch)), dim3(64), kFanoutLdsBytes, stream,
+                     rows, static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), K, nvec, nch,
                      dst_rows, read_src);
   return status();
 }
@@ -223,7 +242,8 @@ int moonep_rows_gather(const int32_t* rows, int64_t n, int K, const void* src, i
   const int nch = (nvec + 63) / 64;
   if (n * nch > INT32_MAX) return kEInval;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)(n * nch)), dim3(64), 0, stream, rows,
+  const int lds = src_rows * (int64_t)row_bytes > kLastLevelCacheBytes ? kGatherLdsBytes : 0;
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)(n * nch)), dim3(64), lds, stream, rows,
                      static_cast<const u32x4*>(src), src_rows, static_cast<u32x4*>(dst), K, nvec,
                      nch, write_dst);
   return status();

@@ -42,15 +42,15 @@ int moonep_stream_copy(const void* src, void* dst, int64_t nbytes, int shape, in
 
 /* Dispatch's mix: for i < n, k < K:  dst row rows[i*K + k] = src row i (read_src != 0), or a
  * fixed pattern (read_src == 0: writes only).  Rows of row_bytes; dst has dst_rows rows.
- * One 64-lane workgroup per (i, 2 KB chunk), non-temporal stores: the dispatch kernel's
- * shape. */
+ * One 64-lane workgroup per (i, 2 KB chunk), non-temporal stores, at most 5 workgroups per
+ * CU: the dispatch kernel's shape and residency. */
 int moonep_rows_fanout(const int32_t* rows, int64_t n, int K, const void* src, void* dst,
                        int64_t dst_rows, int row_bytes, int read_src, hipStream_t stream);
 
 /* Combine's mix: for i < n:  dst row i = XOR over k < K of src row rows[i*K + k]
  * (write_dst != 0), or nothing written (write_dst == 0: reads only).  src has src_rows
- * rows.  One 64-lane workgroup per (i, 1 KB chunk), non-temporal loads and stores: the
- * combine kernel's shape. */
+ * rows.  One 64-lane workgroup per (i, 1 KB chunk), non-temporal loads and stores, at most
+ * 9 workgroups per CU when src exceeds 256 MB: the combine kernel's shape and residency. */
 int moonep_rows_gather(const int32_t* rows, int64_t n, int K, const void* src, int64_t src_rows,
                        void* dst, int row_bytes, int write_dst, hipStream_t stream);
 
