@@ -219,12 +219,17 @@ __global__ __launch_bounds__(kWave) void combine_kernel(const int32_t* __restric
 // combine backward: g_y[dst_row[t,k]] = bf16(w[t,k] * dout[t]);
 //                   dw[t,k] = sum_h dout[t,h] * y[dst_row[t,k],h]   (fp32, fused multiply-add)
 // ---------------------------------------------------------------------------------------
-// One workgroup per token.  Each thread holds U vectors of dout, reads the same vectors of
-// each of the K rows of y, keeps K partial dot products, and writes the scaled dout
-// vectors to the K rows of g_y (g_y may be y itself: each element is read before it is
-// written by the same thread).  The K partials are summed over the wave with lane
-// shuffles, then over the waves in LDS.  KMAX = K when K is a compile-time
-// constant, else MOONEP_MAX_K with the loop bounded by the runtime K.
+// One workgroup per token.  Each thread holds U vectors of dout and takes the K rows of y
+// in groups: it loads the same vectors of every row of the group, waits once, then keeps
+// a partial dot product per row and writes the scaled dout vectors to the group's rows of
+// g_y back to back (g_y may be y itself: each element is read before it is written by
+// the same thread).  Without the single wait the compiler places a wait for every
+// earlier memory operation before each store (vmcnt counts loads and stores alike), and
+// the row-by-row load, wait, store sequence ran at 5.1 TB/s.  The K partials are summed
+// over the wave with lane shuffles, then over the waves in LDS.  KMAX = K when K is a
+// compile-time constant, else MOONEP_MAX_K with the loop bounded by the runtime K.
+constexpr int kBwdGroup = 8;    // rows of y per group (fewer when U > 2 or K is not a constant)
+
 template <int KMAX, int U>
 __global__ __launch_bounds__(1024) void combine_bwd_kernel(const int32_t* __restrict__ dst,
                                                            const float* __restrict__ wts,
@@ -246,28 +251,48 @@ __global__ __launch_bounds__(1024) void combine_bwd_kernel(const int32_t* __rest
       const int v = v0 + u * blockDim.x;
       dv[u] = v < nvec ? __builtin_nontemporal_load(dout + t * nvec + v) : u32x4{0u, 0u, 0u, 0u};
     }
+    // groups of up to 8 rows: every load of the group, one wait, then the group's stores
+    // back to back (a row is read before it is overwritten when g_y is y)
+    constexpr int NG = KMAX <= kBwdGroup && U <= 2 ? KMAX
+                       : KMAX < 4 ? KMAX : KMAX > kBwdGroup && U > 2 ? 2 : 4;
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-      if (k >= K) break;
-      const int row = d[k];
-      if ((unsigned)row >= (unsigned)nrows) continue;     // -1: unmapped
-      const float wk = wt[k];
-      const u32x4* ysrc = y + (int64_t)row * nvec;
-      u32x4* gdst = g_y + (int64_t)row * nvec;
+    for (int k0 = 0; k0 < KMAX; k0 += NG) {
+      if (k0 >= K) break;
+      int row[NG];
+      bool ok[NG];
+      float wk[NG];
+      u32x4 yv[NG][U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int v = v0 + u * blockDim.x;
-        if (v < nvec) {
-          const u32x4 yv = __builtin_nontemporal_load(ysrc + v);
+      for (int j = 0; j < NG; ++j) {
+        const int k = k0 + j;
+        row[j] = k < K ? d[k] : -1;
+        ok[j] = (unsigned)row[j] < (unsigned)nrows;      // -1: unmapped, or past K
+        wk[j] = k < K ? wt[k] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < NG; ++j)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int v = v0 + u * blockDim.x;
+          yv[j][u] = ok[j] && v < nvec ? __builtin_nontemporal_load(y + (int64_t)row[j] * nvec + v)
+                                       : u32x4{0u, 0u, 0u, 0u};
+        }
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+#pragma unroll
+      for (int j = 0; j < NG; ++j) {
+        if (!ok[j]) continue;
+        u32x4* gdst = g_y + (int64_t)row[j] * nvec;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int v = v0 + u * blockDim.x;
+          if (v >= nvec) continue;
           u32x4 g;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float d0 = bf_lo(dv[u][q]), d1 = bf_hi(dv[u][q]);
-            part[k] = __builtin_fmaf(d0, bf_lo(yv[q]), part[k]);
-            part[k] = __builtin_fmaf(d1, bf_hi(yv[q]), part[k]);
-            const float g0 = wk * d0;
-            const float g1 = wk * d1;
-            g[q] = to_bf16(g0) | (to_bf16(g1) << 16);
+            part[k0 + j] = __builtin_fmaf(d0, bf_lo(yv[j][u][q]), part[k0 + j]);
+            part[k0 + j] = __builtin_fmaf(d1, bf_hi(yv[j][u][q]), part[k0 + j]);
+            g[q] = to_bf16(wk[j] * d0) | (to_bf16(wk[j] * d1) << 16);
           }
           __builtin_nontemporal_store(g, gdst + v);
         }
@@ -316,54 +341,69 @@ void launch_combine_bwd_k(const moonep_sizes& s, const int32_t* dst, const float
 // ---------------------------------------------------------------------------------------
 // EPILOGUE: recv[dst_row[t,k]] = stage[t*K + k]  (staging buffer -> final rows)
 // PROLOGUE: stage[t*K + k] = y[dst_row[t,k]]     (final rows -> staging buffer)
-template <int U, bool EPILOGUE>
-__global__ __launch_bounds__(1024) void copy_rows_kernel(const int32_t* __restrict__ dst,
-                                                         const u32x4* __restrict__ src,
-                                                         u32x4* __restrict__ out, int K,
-                                                         int nvec, int nrows) {
-  const int64_t t = blockIdx.x;
+// The dispatch kernel's shape and residency, so that the baseline is as well built as the
+// path it is compared with: one single-wave workgroup per (token, 2 KB chunk); for each
+// group of up to 8 of the token's rows, every load, one wait, then the non-temporal
+// stores back to back.
+template <int KT, bool EPILOGUE>
+__global__ __launch_bounds__(kWave) void copy_rows_kernel(const int32_t* __restrict__ dst,
+                                                          const u32x4* __restrict__ src,
+                                                          u32x4* __restrict__ out, int Krt,
+                                                          int nvec, int nch, int nrows) {
+  const int K = KT > 0 ? KT : Krt;
+  const int64_t t = blockIdx.x / nch;
+  const int c0 = (int)(blockIdx.x - t * nch) * kDispChunk + (int)threadIdx.x;
   const int32_t* d = dst + t * K;
-  for (int k = 0; k < K; ++k) {
-    const int r = d[k];
-    if ((unsigned)r >= (unsigned)nrows) continue;      // -1: unmapped
-    const int64_t srow = EPILOGUE ? t * K + k : r;
-    const int64_t drow = EPILOGUE ? r : t * K + k;
-    const u32x4* sp = src + srow * nvec;
-    u32x4* op = out + drow * nvec;
-    for (int v0 = threadIdx.x; v0 < nvec; v0 += blockDim.x * U) {
-      u32x4 buf[U];
+  constexpr int G = KT > 0 && KT < 8 ? KT : 8;
+  for (int k0 = 0; k0 < K; k0 += G) {
+    int64_t srow[G], drow[G];
+    bool ok[G];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int v = v0 + u * blockDim.x;
-        if (v < nvec) buf[u] = sp[v];
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int v = v0 + u * blockDim.x;
-        if (v < nvec) op[v] = buf[u];
-      }
+    for (int j = 0; j < G; ++j) {
+      const int k = k0 + j;
+      const int r = k < K ? d[k] : -1;
+      ok[j] = (unsigned)r < (unsigned)nrows;          // -1: unmapped, or past K
+      srow[j] = EPILOGUE ? t * K + k : r;
+      drow[j] = EPILOGUE ? r : t * K + k;
     }
+    u32x4 buf[G][kDispU];
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int u = 0; u < kDispU; ++u) {
+        const int v = c0 + u * kWave;
+        if (ok[j] && v < nvec) buf[j][u] = src[srow[j] * nvec + v];
+      }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int u = 0; u < kDispU; ++u) {
+        const int v = c0 + u * kWave;
+        if (ok[j] && v < nvec) __builtin_nontemporal_store(buf[j][u], out + drow[j] * nvec + v);
+      }
   }
+}
+
+template <int KT, bool EPILOGUE>
+void launch_copy_rows_k(const moonep_sizes& s, const int32_t* dst, const uint16_t* src,
+                        uint16_t* out, int nvec, int nch, hipStream_t st) {
+  hipLaunchKernelGGL((copy_rows_kernel<KT, EPILOGUE>), dim3((unsigned)(s.T * nch)), dim3(kWave),
+                     kDispLdsBytes, st, dst, reinterpret_cast<const u32x4*>(src),
+                     reinterpret_cast<u32x4*>(out), s.K, nvec, nch, (int)s.recv_rows);
 }
 
 template <bool EPILOGUE>
 void launch_copy_rows(const moonep_sizes& s, const int32_t* dst, const uint16_t* src, uint16_t* out,
                       int nvec, hipStream_t st) {
-  int threads = 64, u = 1;
-  row_shape(nvec, 8, 7, &threads, &u);
-  const dim3 grid((unsigned)s.T), block(threads);
-  const u32x4* sv = reinterpret_cast<const u32x4*>(src);
-  u32x4* ov = reinterpret_cast<u32x4*>(out);
-  const int nrows = (int)s.recv_rows;
-  switch (u) {
-    case 1: hipLaunchKernelGGL((copy_rows_kernel<1, EPILOGUE>), grid, block, 0, st, dst, sv, ov, s.K, nvec, nrows); break;
-    case 2: hipLaunchKernelGGL((copy_rows_kernel<2, EPILOGUE>), grid, block, 0, st, dst, sv, ov, s.K, nvec, nrows); break;
-    case 3: hipLaunchKernelGGL((copy_rows_kernel<3, EPILOGUE>), grid, block, 0, st, dst, sv, ov, s.K, nvec, nrows); break;
-    case 4: hipLaunchKernelGGL((copy_rows_kernel<4, EPILOGUE>), grid, block, 0, st, dst, sv, ov, s.K, nvec, nrows); break;
-    case 5: hipLaunchKernelGGL((copy_rows_kernel<5, EPILOGUE>), grid, block, 0, st, dst, sv, ov, s.K, nvec, nrows); break;
-    case 6: hipLaunchKernelGGL((copy_rows_kernel<6, EPILOGUE>), grid, block, 0, st, dst, sv, ov, s.K, nvec, nrows); break;
-    case 7: hipLaunchKernelGGL((copy_rows_kernel<7, EPILOGUE>), grid, block, 0, st, dst, sv, ov, s.K, nvec, nrows); break;
-    default: hipLaunchKernelGGL((copy_rows_kernel<8, EPILOGUE>), grid, block, 0, st, dst, sv, ov, s.K, nvec, nrows); break;
+  const int nch = (nvec + kDispChunk - 1) / kDispChunk;
+  switch (s.K) {
+    case 1: launch_copy_rows_k<1, EPILOGUE>(s, dst, src, out, nvec, nch, st); break;
+    case 2: launch_copy_rows_k<2, EPILOGUE>(s, dst, src, out, nvec, nch, st); break;
+    case 4: launch_copy_rows_k<4, EPILOGUE>(s, dst, src, out, nvec, nch, st); break;
+    case 6: launch_copy_rows_k<6, EPILOGUE>(s, dst, src, out, nvec, nch, st); break;
+    case 8: launch_copy_rows_k<8, EPILOGUE>(s, dst, src, out, nvec, nch, st); break;
+    default: launch_copy_rows_k<0, EPILOGUE>(s, dst, src, out, nvec, nch, st); break;
   }
 }
 
@@ -399,6 +439,7 @@ __global__ __launch_bounds__(kCopyThreads) void prefetch_kernel(const int32_t* _
       const int64_t i = c * kCopyChunk + u * kCopyThreads + threadIdx.x;
       if (i < wv) v[u] = __builtin_nontemporal_load(src + i);
     }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);     // then the stores issue back to back
 #pragma unroll
     for (int u = 0; u < kCopyU; ++u) {
       const int64_t i = c * kCopyChunk + u * kCopyThreads + threadIdx.x;
