@@ -19,6 +19,7 @@ constexpr int kPlanThreads = 1024;          // the single planner workgroup
 constexpr int kPieceInts = 8;               // e, r, slot, cnt, start, fbpos, row0, pad
 constexpr int kColumnBudget = 32768;        // blocks x experts the planner scans in registers
 constexpr int kMapChunks = 8;               // 64-assignment chunks per map wave, at most
+constexpr int kWsCtl = 64;                  // control words at the head of the plan workspace
 
 // header words
 enum Hdr : int {
@@ -76,13 +77,15 @@ inline int fill_sizes(int R, int E, int K, int S, int slots, moonep_sizes* s) {
   s->o_dst_row = o;     o += align64(A);
   s->o_w = o;           o += align64(A);
   s->plan_bytes = o * 4;
-  // workspace: per-block expert counts [nblk][E] (overwritten by the planner with
-  // per-block bases), per-block first bad index [nblk], per-wave prefixes inside each
-  // block [nblk][kMapWaves][E], and, when a histogram wave's 64*m assignments are split
-  // into Q > 1 map sub-blocks, the wave's running counts at each inner sub-block boundary
-  // [nblk][kMapWaves][Q-1][E]
+  // workspace: kWsCtl control words (word 0: the histogram workgroups' arrival count,
+  // zero between calls), then per-block expert counts [nblk][E] (overwritten by the
+  // planner with per-block bases), per-block first bad index [nblk], per-wave prefixes
+  // inside each block [nblk][kMapWaves][E], and, when a histogram wave's 64*m assignments
+  // are split into Q > 1 map sub-blocks, the wave's running counts at each inner
+  // sub-block boundary [nblk][kMapWaves][Q-1][E].  The offsets below count from the end
+  // of the control words.
   const int64_t Q = m > kMapChunks ? m / kMapChunks : 1;
-  s->workspace_bytes = (align64((int64_t)s->nblk * E) + align64(s->nblk) +
+  s->workspace_bytes = (kWsCtl + align64((int64_t)s->nblk * E) + align64(s->nblk) +
                         align64((int64_t)s->nblk * kMapWaves * E) +
                         align64((int64_t)s->nblk * kMapWaves * (Q - 1) * E)) * 4;
   return MOONEP_OK;

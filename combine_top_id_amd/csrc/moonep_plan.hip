@@ -8,25 +8,25 @@
 // plus alignment padding buffers.
 //
 // Assignments are cut into blocks of `blk` = kMapThreads * M; block b is counted by one
-// workgroup, whose wave w owns the contiguous sub-block of 64*M assignments starting at
-// b*blk + w*64*M.  Three launches on the caller's stream:
-//   1. hist_kernel     per block: one LDS histogram per wave -> the block's expert counts
-//                      and, per wave, the count of earlier waves of the block (and, for
-//                      waves of more than 8 chunks, the wave's running counts at each
-//                      8-chunk boundary); the first invalid id of the block.
-//   2. planner_kernel  one workgroup: per-block bases (exclusive scan of the counts over
-//                      blocks), expert loads, per-rank excess and deficit, shedding,
-//                      greedy placement (wave 0, lane r = rank r: a parallel cut of the
-//                      shed stream up to the first expert that would overfill a slot
-//                      budget, then one expert at a time), buffer layout (one block-wide
-//                      scan), piece rows, statistics.  Everything stays in LDS until one
-//                      final write of the plan.
-//   3. map_kernel      one single-wave workgroup per map sub-block (a histogram wave's
-//                      sub-block, or a part of at most 8 chunks of it, whose starting
-//                      counts the histogram wave recorded): the stable rank j of each
-//                      assignment among its expert's assignments (per-id LDS peer masks
-//                      and an LDS counter per expert), then its row; copies the top-K
-//                      weights.
+// logical workgroup of kMapWaves waves, whose wave w owns the contiguous sub-block of 64*M
+// assignments starting at b*blk + w*64*M.  Two launches on the caller's stream:
+//   1. hist_plan_kernel  two logical blocks per workgroup of kPlanThreads.
+//        histogram: one LDS histogram per wave -> the block's expert counts and, per
+//          wave, the count of earlier waves of the block (and, for waves of more than 8
+//          chunks, the wave's running counts at each 8-chunk boundary); the first
+//          invalid id of the block.
+//        planner, in the workgroup that finishes its histogram last: per-block bases
+//          (exclusive scan of the counts over blocks), expert loads, per-rank excess and
+//          deficit, shedding, greedy placement (wave 0, lane r = rank r: a parallel cut
+//          of the shed stream up to the first expert that would overfill a slot budget,
+//          then one expert at a time), buffer layout (one block-wide scan), piece rows,
+//          statistics.  Everything stays in LDS until one final write of the plan.
+//   2. map_kernel        one single-wave workgroup per map sub-block (a histogram wave's
+//                        sub-block, or a part of at most 8 chunks of it, whose starting
+//                        counts the histogram wave recorded): the stable rank j of each
+//                        assignment among its expert's assignments (per-id LDS peer masks
+//                        and an LDS counter per expert), then its row; copies the top-K
+//                        weights.
 #include <climits>
 
 #include "moonep_internal.h"
@@ -86,26 +86,28 @@ __device__ __forceinline__ int count_le(const int32_t* a, int n, int x) {
 __device__ __forceinline__ int align_rows(int n) { return (n + kRowAlign - 1) / kRowAlign * kRowAlign; }
 
 // ---------------------------------------------------------------------------------------
-// 1. per-block histogram
+// 1. per-block histogram (device function; the launch is hist_plan_kernel below)
 // ---------------------------------------------------------------------------------------
+// One logical block of kMapWaves waves (tid in [0, kMapThreads)) counts blk assignments
+// into its own LDS histograms `lds_blk` ([kMapWaves][E]); b >= nblk counts nothing but
+// still takes part in the workgroup's barriers.
 template <int M>
-__global__ __launch_bounds__(kMapThreads) void hist_kernel(const int32_t* __restrict__ ids,
-                                                           int32_t* __restrict__ ws,
-                                                           const moonep_sizes s) {
-  extern __shared__ int32_t lds[];          // [kMapWaves][E]
-  __shared__ int bad;
+__device__ __forceinline__ void hist_block(const int32_t* __restrict__ ids, int32_t* __restrict__ ws,
+                                           const moonep_sizes& s, int b, int tid, int32_t* lds_blk,
+                                           int* bad) {
   const int E = s.E;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int64_t i_wave = (int64_t)blockIdx.x * s.blk + (int64_t)wave * (64 * M);
+  const bool active = b < s.nblk;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int64_t i_wave = (int64_t)b * s.blk + (int64_t)wave * (64 * M);
   int idv[M];
 #pragma unroll
   for (int c = 0; c < M; ++c) {
     const int64_t i = i_wave + c * 64 + lane;
-    idv[c] = i < s.A ? ids[i] : 0;
+    idv[c] = active && i < s.A ? ids[i] : 0;
   }
-  int32_t* mine = lds + wave * E;
+  int32_t* mine = lds_blk + wave * E;
   for (int e = lane; e < E; e += 64) mine[e] = 0;
-  if (tid == 0) bad = INT_MAX;
+  if (tid == 0) *bad = INT_MAX;
   __syncthreads();
   int mybad = INT_MAX;
   // Q > 1: the map splits this wave's chunks into Q sub-blocks of MC chunks, and needs
@@ -113,15 +115,15 @@ __global__ __launch_bounds__(kMapThreads) void hist_kernel(const int32_t* __rest
   // effect in program order, so the reads see every earlier add of the wave)
   constexpr int MC = M < kMapChunks ? M : kMapChunks;
   constexpr int Q = M / MC;
-  int32_t* snap = ws + ws_snap(s) + ((int64_t)blockIdx.x * kMapWaves + wave) * (Q - 1) * E;
+  int32_t* snap = ws + ws_snap(s) + ((int64_t)b * kMapWaves + wave) * (Q - 1) * E;
 #pragma unroll
   for (int c = 0; c < M; ++c) {
-    if (Q > 1 && c > 0 && c % MC == 0) {
+    if (Q > 1 && active && c > 0 && c % MC == 0) {
       int32_t* sn = snap + (int64_t)(c / MC - 1) * E;
       for (int e = lane; e < E; e += 64) sn[e] = mine[e];
     }
     const int64_t i = i_wave + c * 64 + lane;
-    if (i < s.A) {
+    if (active && i < s.A) {
       const int id = idv[c];
       if ((unsigned)id < (unsigned)E)
         atomicAdd(&mine[id], 1);
@@ -129,25 +131,26 @@ __global__ __launch_bounds__(kMapThreads) void hist_kernel(const int32_t* __rest
         mybad = min(mybad, (int)i);
     }
   }
-  if (mybad != INT_MAX) atomicMin(&bad, mybad);
+  if (mybad != INT_MAX) atomicMin(bad, mybad);
   __syncthreads();
-  int32_t* cnt = ws + (int64_t)blockIdx.x * E;
-  int32_t* sub = ws + ws_sub(s) + (int64_t)blockIdx.x * kMapWaves * E;
+  if (!active) return;
+  int32_t* cnt = ws + (int64_t)b * E;
+  int32_t* sub = ws + ws_sub(s) + (int64_t)b * kMapWaves * E;
   for (int e = tid; e < E; e += kMapThreads) {
     int acc = 0;
 #pragma unroll
     for (int v = 0; v < kMapWaves; ++v) {
-      const int c = lds[v * E + e];
+      const int c = lds_blk[v * E + e];
       sub[v * E + e] = acc;
       acc += c;
     }
     cnt[e] = acc;
   }
-  if (tid == 0) ws[ws_bad(s) + blockIdx.x] = bad;
+  if (tid == 0) ws[ws_bad(s) + b] = *bad;
 }
 
 // ---------------------------------------------------------------------------------------
-// 2. the planner (one workgroup of kPlanThreads)
+// 2. the planner (device function of one workgroup of kPlanThreads)
 // ---------------------------------------------------------------------------------------
 
 // Does expert a come before expert b in (load descending, id ascending) order?
@@ -157,10 +160,8 @@ __device__ __forceinline__ bool before(int la, int a, int lb, int b) {
 
 constexpr int kColRegs = 32;   // block counts a column thread keeps in registers
 
-__global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restrict__ plan,
-                                                               int32_t* __restrict__ ws,
-                                                               const moonep_sizes s) {
-  extern __shared__ int32_t lds[];
+__device__ __forceinline__ void planner_block(int32_t* __restrict__ plan, int32_t* __restrict__ ws,
+                                              const moonep_sizes& s, int32_t* lds) {
   const int E = s.E, R = s.R, E_loc = s.E_loc, C = s.C, slots = s.slots, G = s.G;
   const int NvS = s.NvS, PM = s.P_max;
   int32_t* load_s = lds;            // [E]
@@ -648,6 +649,50 @@ __global__ __launch_bounds__(kPlanThreads) void planner_kernel(int32_t* __restri
 }
 
 // ---------------------------------------------------------------------------------------
+// 1+2. histogram and planner in one launch
+// ---------------------------------------------------------------------------------------
+// Each workgroup of kPlanThreads holds two logical histogram blocks (waves 0-7 and 8-15;
+// the block and wave numbering the map kernel reads is unchanged).  A workgroup that has
+// written its counts makes them visible device-wide, then counts itself in an arrival
+// word; the workgroup that arrives last sees every count and runs the planner.  Nothing
+// waits on another workgroup, so no residency assumption is made, and the kernel
+// boundary between histogram and planner (3.3 us at DeepSeek-V3 shape, device
+// timestamps) disappears.  The arrival word is word 0 of `ctl`; the last workgroup
+// returns it to zero, so it is zero at every call as long as the workspace was zero
+// before its first use.
+// A device-scope fence on gfx950 writes back and invalidates the XCD's whole L2, so only
+// one wave per workgroup fences, after every wave has waited for its own stores: with
+// every wave fencing the kernel took 37.7 us instead of 16.7 us (rocprofv3, DeepSeek-V3
+// shape; the two kernels it replaces took 3.7 + 12.2 us plus the boundary).
+template <int M>
+__global__ __launch_bounds__(kPlanThreads) void hist_plan_kernel(const int32_t* __restrict__ ids,
+                                                                 int32_t* __restrict__ plan,
+                                                                 int32_t* __restrict__ ctl,
+                                                                 int32_t* __restrict__ ws,
+                                                                 const moonep_sizes s) {
+  extern __shared__ int32_t lds[];
+  __shared__ int bad2[2];
+  __shared__ int last;
+  const int half = (int)threadIdx.x / kMapThreads;
+  hist_block<M>(ids, ws, s, (int)blockIdx.x * 2 + half, (int)threadIdx.x - half * kMapThreads,
+                lds + half * kMapWaves * s.E, &bad2[half]);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores have reached the L2
+  __syncthreads();                    // ... and every other wave's
+  if (threadIdx.x == 0) {
+    __threadfence();                  // one wave releases them device-wide
+    last = atomicAdd(&ctl[0], 1) == (int)gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!last) return;
+  if (threadIdx.x == 0) {
+    __threadfence();                  // and, in the last workgroup, acquires the others'
+    atomicExch(&ctl[0], 0);
+  }
+  __syncthreads();
+  planner_block(plan, ws, s, lds);
+}
+
+// ---------------------------------------------------------------------------------------
 // 3. token -> row map
 // ---------------------------------------------------------------------------------------
 
@@ -822,9 +867,12 @@ hipError_t launch_map(const moonep_sizes& s, const int32_t* ids, const float* w,
 }
 
 template <int M>
-hipError_t launch_hist(const moonep_sizes& s, const int32_t* ids, int32_t* ws, hipStream_t st) {
-  hipLaunchKernelGGL(hist_kernel<M>, dim3(s.nblk), dim3(kMapThreads),
-                     (size_t)kMapWaves * s.E * sizeof(int32_t), st, ids, ws, s);
+hipError_t launch_hist_plan(const moonep_sizes& s, const int32_t* ids, int32_t* plan, int32_t* ctl,
+                            int32_t* ws, hipStream_t st) {
+  const size_t hist_lds = (size_t)2 * kMapWaves * s.E * sizeof(int32_t);
+  const size_t plan_lds = (size_t)(7 * s.E + max(kPlanThreads, 7 * s.P_max)) * sizeof(int32_t);
+  hipLaunchKernelGGL(hist_plan_kernel<M>, dim3((unsigned)((s.nblk + 1) / 2)), dim3(kPlanThreads),
+                     hist_lds > plan_lds ? hist_lds : plan_lds, st, ids, plan, ctl, ws, s);
   return hipGetLastError();
 }
 
@@ -832,26 +880,25 @@ hipError_t launch_hist(const moonep_sizes& s, const int32_t* ids, int32_t* ws, h
 
 hipError_t launch_plan(const moonep_sizes& s, const int32_t* ids, const float* w,
                        int32_t* plan, int32_t* ws, hipStream_t st) {
+  // workspace: kWsCtl control words (the arrival word first), then the per-block arrays
+  int32_t* ctl = ws;
+  int32_t* body = ws + kWsCtl;
   hipError_t err;
   switch (s.blk / kMapThreads) {
-    case 1: err = launch_hist<1>(s, ids, ws, st); break;
-    case 2: err = launch_hist<2>(s, ids, ws, st); break;
-    case 4: err = launch_hist<4>(s, ids, ws, st); break;
-    case 8: err = launch_hist<8>(s, ids, ws, st); break;
-    case 16: err = launch_hist<16>(s, ids, ws, st); break;
-    case 32: err = launch_hist<32>(s, ids, ws, st); break;
+    case 1: err = launch_hist_plan<1>(s, ids, plan, ctl, body, st); break;
+    case 2: err = launch_hist_plan<2>(s, ids, plan, ctl, body, st); break;
+    case 4: err = launch_hist_plan<4>(s, ids, plan, ctl, body, st); break;
+    case 8: err = launch_hist_plan<8>(s, ids, plan, ctl, body, st); break;
+    case 16: err = launch_hist_plan<16>(s, ids, plan, ctl, body, st); break;
+    case 32: err = launch_hist_plan<32>(s, ids, plan, ctl, body, st); break;
     default: return hipErrorInvalidValue;
   }
   if (err != hipSuccess) return err;
-  const size_t plds = (size_t)(7 * s.E + max(kPlanThreads, 7 * s.P_max)) * sizeof(int32_t);
-  hipLaunchKernelGGL(planner_kernel, dim3(1), dim3(kPlanThreads), plds, st, plan, ws, s);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
   switch (map_chunks(s)) {
-    case 1: return launch_map<1>(s, ids, w, plan, ws, st);
-    case 2: return launch_map<2>(s, ids, w, plan, ws, st);
-    case 4: return launch_map<4>(s, ids, w, plan, ws, st);
-    case 8: return launch_map<8>(s, ids, w, plan, ws, st);
+    case 1: return launch_map<1>(s, ids, w, plan, body, st);
+    case 2: return launch_map<2>(s, ids, w, plan, body, st);
+    case 4: return launch_map<4>(s, ids, w, plan, body, st);
+    case 8: return launch_map<8>(s, ids, w, plan, body, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -148,9 +148,10 @@ class Plan:
         return self.array("w", self.sz.A).view(torch.float32).view(self.sz.T, self.sz.K)
 
 
-def _blob(nbytes, device):
+def _blob(nbytes, device, zero=False):
     # int32 elements; torch's caching allocator returns 256-byte aligned blocks
-    t = torch.empty((nbytes + 3) // 4, dtype=torch.int32, device=device)
+    n = (nbytes + 3) // 4
+    t = (torch.zeros if zero else torch.empty)(n, dtype=torch.int32, device=device)
     assert t.data_ptr() % 256 == 0
     return t
 
@@ -165,8 +166,9 @@ def moonep_plan(topk_ids, topk_w, R, E, K, S, slots, plan=None, stream=None) -> 
         raise MoonepError("topk_ids / topk_w must hold R*S*K elements")
     if plan is None or plan.workspace is None or plan.sz.plan_bytes != sz.plan_bytes or \
             plan.sz.workspace_bytes != sz.workspace_bytes:
+        # the workspace starts zero-filled; every plan call leaves it so
         plan = Plan(sz, _blob(sz.plan_bytes, topk_ids.device),
-                    _blob(sz.workspace_bytes, topk_ids.device))
+                    _blob(sz.workspace_bytes, topk_ids.device, zero=True))
     plan.sz = sz
     _check(lib().moonep_plan(ids_p, w_p, R, E, K, S, slots,
                              ctypes.c_void_p(plan.blob.data_ptr()),

@@ -111,8 +111,12 @@ int moonep_query(int R, int E, int K, int S, int slots, moonep_sizes* out);
  *   topk_ids   device int32 [T, K] row-major, ranks contiguous (token t from rank t/S)
  *   topk_w     device fp32  [T, K]; copied into the plan, so combine needs no weights
  *   plan_dev   device blob of moonep_sizes.plan_bytes, 256-byte aligned
- *   workspace  device scratch of moonep_sizes.workspace_bytes, 256-byte aligned; free
- *              for reuse once the plan's kernels have run on `stream`
+ *   workspace  device scratch of moonep_sizes.workspace_bytes, 256-byte aligned,
+ *              zero-filled before its first use: its first word counts the planning
+ *              workgroups as they finish, and every call leaves it at zero again, so a
+ *              workspace reused call after call (for any sizes) needs no clearing.  Free
+ *              for other use once the plan's kernels have run on `stream`; two calls whose
+ *              kernels overlap in time must not share a workspace
  *   desc       host handle, filled synchronously (sizes + plan_dev)
  *
  * Boundary note.  The plan is a device blob, as in a blob-only signature, but the call also
@@ -152,7 +156,9 @@ int moonep_plan(const int32_t* topk_ids, const float* topk_w, int R, int E, int 
  * Every call on one GPU shares that GPU's array: two of these calls whose kernels overlap
  * in time on the same GPU (different streams, or different host threads without ordering)
  * race and may both produce wrong plans.  Calls ordered on one stream are safe.  The array
- * need not start at zero and keeps the last call's contents. */
+ * is zero when the library is loaded; every call leaves its first word (the planning
+ * workgroups' arrival count) at zero again and the rest holding the last call's
+ * contents. */
 int moonep_plan_noalloc(const int32_t* topk_ids, const float* topk_w, int R, int E, int K, int S,
                         int slots, void* plan_dev, moonep_plan_desc* desc, hipStream_t stream);
 

@@ -73,6 +73,7 @@ static int gpu_run(void) {
   HIPOK(hipMalloc(&d_w, sizeof(float) * T * K));
   HIPOK(hipMalloc(&d_plan, (size_t)s.plan_bytes));
   HIPOK(hipMalloc(&d_ws, (size_t)s.workspace_bytes));
+  HIPOK(hipMemset(d_ws, 0, (size_t)s.workspace_bytes));   /* zero before its first use */
   HIPOK(hipMalloc(&d_x, sizeof(uint16_t) * T * H));
   HIPOK(hipMalloc(&d_recv, sizeof(uint16_t) * (size_t)s.recv_rows * H));
   HIPOK(hipMalloc(&d_out, sizeof(uint16_t) * T * H));

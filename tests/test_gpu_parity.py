@@ -345,6 +345,28 @@ def test_plan_is_deterministic_and_reusable():
     assert torch.equal(o1.float(), x.float())
 
 
+def test_one_workspace_serves_every_size():
+    """One zero-filled workspace, reused call after call for problems of different sizes
+    (the workgroup counts of the planning launch differ): every plan equals the oracle's,
+    and the arrival word at the workspace's head is zero again after each call."""
+    cases = [(DSV3, 0), (TINY, 0), (SMALL, 0), (DECODE, 1), (TINY, 0), (DSV3, 3)]
+    sizes = [M.moonep_query(wl.R, wl.E, wl.K, wl.S, wl.slots) for wl, _ in cases]
+    ws = torch.zeros(max(sz.workspace_bytes for sz in sizes) // 4 + 64, dtype=torch.int32,
+                     device="cuda")
+    for (wl, mi), sz in zip(cases, sizes):
+        say(f"shared workspace: {wl.name} maxvio {wl.maxvio[mi]}")
+        ids, w, _, _ = make_routing(wl.R, wl.E, wl.K, wl.S, wl.maxvio[mi], wl.seed(mi),
+                                    device="cuda")
+        blob = torch.empty(sz.plan_bytes // 4, dtype=torch.int32, device="cuda")
+        plan = M.moonep_plan(ids, w, wl.R, wl.E, wl.K, wl.S, wl.slots,
+                             plan=M.Plan(sz, blob, ws[: sz.workspace_bytes // 4]))
+        assert plan.workspace.data_ptr() == ws.data_ptr()
+        ids_np = ids.cpu().numpy()
+        p = O.plan(ids_np, wl.R, wl.E, wl.K, wl.S, wl.slots)
+        assert_plan_matches(read_plan(plan), p, O.slot_map(p, ids_np))
+        assert int(ws[0].item()) == 0
+
+
 # ----------------------------------------------------------------------------------------
 # full-size workloads: whole plan, dst_row, every dispatched row, padding, every combined
 # token and every reduced expert
