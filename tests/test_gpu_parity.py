@@ -367,6 +367,42 @@ def test_one_workspace_serves_every_size():
         assert int(ws[0].item()) == 0
 
 
+def test_plan_repeats_identically_over_random_sizes():
+    """Many problem sizes, so the planning launch runs with anything from one to a few
+    hundred workgroups: planning four times into the same blob and workspace gives the same
+    blob each time, the arrival word is zero after each call, and the small problems match
+    the oracle."""
+    import random
+    rng = random.Random(20260001)
+    done = 0
+    while done < 150:
+        R = rng.choice([1, 2, 4, 8, 16, 32, 64])
+        E = R * rng.choice([1, 2, 4, 6, 8, 16, 24, 32])
+        if E > 1024:
+            continue
+        K = rng.randint(1, min(E, 10))
+        S = rng.choice([1, 7, 64, 300, 1024, 4096])
+        if R * S * K > 2_000_000:
+            continue
+        slots = rng.choice([0, 1, 2, 4, 8, E // R])
+        mv = rng.choice([0.2, 1.0, 5.0, 20.0])
+        ids, w, _, _ = make_routing(R, E, K, S, mv, rng.randint(0, 10 ** 6), device="cuda")
+        plan, first = None, None
+        for rep in range(4):
+            plan = M.moonep_plan(ids, w, R, E, K, S, slots, plan=plan)
+            torch.cuda.synchronize()
+            assert int(plan.workspace[0].item()) == 0
+            if first is None:
+                first = plan.blob.clone()
+                if R * S * K <= 20000:
+                    ids_np = ids.cpu().numpy()
+                    p = O.plan(ids_np, R, E, K, S, slots)
+                    assert_plan_matches(read_plan(plan), p, O.slot_map(p, ids_np))
+            else:
+                assert torch.equal(plan.blob, first), (R, E, K, S, slots, mv, rep)
+        done += 1
+
+
 # ----------------------------------------------------------------------------------------
 # full-size workloads: whole plan, dst_row, every dispatched row, padding, every combined
 # token and every reduced expert
