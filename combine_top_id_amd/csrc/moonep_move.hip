@@ -51,10 +51,12 @@ void row_shape(int nvec, int umax, int upref, int* threads, int* u) {
 // wave covers 1 KB contiguous), then stores each of them to the token's K destination
 // rows, vector by vector, with non-temporal stores.  Measured on MI355X, interleaved A/B
 // in one process on DeepSeek-V3-, Kimi- and decode-shaped routing: one wave per 2 KB
-// chunk is 2-5% faster than one 448-thread workgroup per token, non-temporal stores add
-// 2-4% on top, and a token-major launch order beats chunk-major or XCD-local orders.
-// A workgroup of one wave starts as soon as any wave slot of a CU frees, so the CUs stay
-// full of short-lived waves; larger workgroups wait for several free slots at once.
+// chunk is 2-5% faster than one 448-thread workgroup per token, and a token-major launch
+// order beats chunk-major or XCD-local orders.  Plain stores run within 1% of
+// non-temporal ones here, but leave dirty lines in the caches that cost the following
+// combine 2-7%.  A workgroup of one wave starts as soon as any wave slot of a CU frees,
+// so the CUs stay full of short-lived waves; larger workgroups wait for several free
+// slots at once (2-, 7-wave workgroups and 2-3 tokens per wave measured 2-20% slower).
 //
 // One explicit wait separates the loads from the stores.  gfx9 counts stores in the
 // same vmcnt counter as loads, and the loads and stores here sit under conditions (a
