@@ -68,7 +68,8 @@ def fanout(rows, K, src, dst, read_src=True):
     """dst[rows[i*K + k]] = src[i] (or a pattern when read_src is False); 2-D row tensors."""
     n = rows.numel() // K
     assert rows.dtype == torch.int32 and rows.is_contiguous()
-    assert (not read_src) or src.shape[0] >= n
+    assert (not read_src) or (src.shape[0] >= n and
+                              src.shape[1] * src.element_size() == dst.shape[1] * dst.element_size())
     _check(lib().moonep_rows_fanout(_p(rows), n, K, _p(src) if read_src else ctypes.c_void_p(0),
                                     _p(dst), dst.shape[0], dst.shape[1] * dst.element_size(),
                                     int(read_src), _s(dst)), "rows_fanout")
@@ -78,6 +79,7 @@ def gather(rows, K, src, dst, write_dst=True):
     """dst[i] = XOR_k src[rows[i*K + k]] (or nothing written when write_dst is False)."""
     n = rows.numel() // K
     assert rows.dtype == torch.int32 and rows.is_contiguous() and dst.shape[0] >= n
+    assert src.shape[1] * src.element_size() == dst.shape[1] * dst.element_size()
     _check(lib().moonep_rows_gather(_p(rows), n, K, _p(src), src.shape[0], _p(dst),
                                     src.shape[1] * src.element_size(), int(write_dst), _s(src)),
            "rows_gather")
