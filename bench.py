@@ -95,7 +95,7 @@ def measured_traffic(kernel_prefix, workload):
     return None
 
 
-def cpu_baseline(wl, ids_np, w_np, x_np, home=None, rep=None, budget_s=15.0):
+def cpu_baseline(wl, ids_np, w_np, x_np, home=None, rep=None, budget_s=20.0):
     """The oracle, as it stands, on a bounded sample of the same workload: each stage timed
     on its own (time.perf_counter, median of 3).  Plan and slot map run on the whole batch;
     dispatch and combine on its first n tokens, n sized to fit the time budget; the
@@ -116,9 +116,10 @@ def cpu_baseline(wl, ids_np, w_np, x_np, home=None, rep=None, budget_s=15.0):
     t_map, dst = med3(lambda: O.slot_map(p, ids_np))
     rows_total = wl.R * p.sz.NvS
 
-    # size the dispatch+combine sample: one probe on 512 tokens, then n tokens so that
-    # three repetitions of both stages take about budget_s
-    probe = min(512, wl.T)
+    # size the dispatch+combine sample: one probe on 2048 tokens (smaller probes carry
+    # more fixed cost per token), then n tokens so that three repetitions of both stages
+    # take about budget_s
+    probe = min(2048, wl.T)
     t = time.perf_counter()
     r = O.dispatch(dst[:probe], x_np[:probe], rows_total)
     O.combine(dst[:probe], w_np[:probe], r)
