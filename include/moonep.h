@@ -27,10 +27,11 @@
  *     (EINVAL, ELIMIT, EALIGN, EPLAN) are found on the host and nothing is enqueued; an
  *     EHIP from a call that launches several kernels (moonep_plan, the staged calls) can
  *     follow launches of that call that were already enqueued.  Each call clears the
- *     thread's earlier HIP error before launching, so an EHIP is its own.  Data errors found on the device (an expert id outside
- *     [0, E)) are never reported by a return code: they set the plan's status word,
- *     read with moonep_plan_status; such a plan maps nothing (every dst_row is -1),
- *     dispatch then writes nothing, combine writes zero rows and reduce adds nothing.
+ *     thread's earlier HIP error before launching, so an EHIP is its own.  Data errors
+ *     found on the device (an expert id outside [0, E)) are never reported by a return
+ *     code: they set the plan's status word, read with moonep_plan_status; such a plan
+ *     maps nothing (every dst_row is -1), dispatch then writes nothing, combine writes
+ *     zero rows and reduce adds nothing.
  *   - Calls are thread-safe; the library has no global mutable state apart from
  *     moonep_plan_noalloc's per-GPU workspace array (see there).
  */
