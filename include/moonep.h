@@ -115,9 +115,11 @@ int moonep_query(int R, int E, int K, int S, int slots, moonep_sizes* out);
  *   workspace  device scratch of moonep_sizes.workspace_bytes, 256-byte aligned,
  *              zero-filled before its first use: its first word counts the planning
  *              workgroups as they finish, and every call leaves it at zero again, so a
- *              workspace reused call after call (for any sizes) needs no clearing.  Free
- *              for other use once the plan's kernels have run on `stream`; two calls whose
- *              kernels overlap in time must not share a workspace
+ *              workspace reused call after call (for any sizes) needs no clearing.  A
+ *              workspace whose first word is not zero leaves the plan undefined (no
+ *              fault: every later kernel bounds its row indices).  Free for other use
+ *              once the plan's kernels have run on `stream`; two calls whose kernels
+ *              overlap in time must not share a workspace
  *   desc       host handle, filled synchronously (sizes + plan_dev)
  *
  * Boundary note.  The plan is a device blob, as in a blob-only signature, but the call also
