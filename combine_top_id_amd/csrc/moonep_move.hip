@@ -26,6 +26,14 @@ __device__ __forceinline__ unsigned int to_bf16(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Counts and piece ranges read from a plan are clamped to the tables they index: a blob
+// that no plan call finished writing can hold anything, and every read stays inside it.
+__device__ __forceinline__ int clamp_count(int n, int max_n) { return min(max(n, 0), max_n); }
+__device__ __forceinline__ void piece_range(int first, int count, int pmax, int* q0, int* q1) {
+  *q0 = clamp_count(first, pmax);
+  *q1 = *q0 + clamp_count(count, pmax - *q0);
+}
+
 // Threads per workgroup (a multiple of 64, at most 1024) and vectors per thread (at most
 // umax) for a row of nvec 16-byte vectors: the fewest idle lanes first, then the vectors
 // per thread closest to upref, then the most threads.
@@ -422,7 +430,7 @@ __global__ __launch_bounds__(kCopyThreads) void prefetch_kernel(const int32_t* _
                                                                 const u32x4* __restrict__ home,
                                                                 u32x4* __restrict__ slotw,
                                                                 int64_t wv, const moonep_sizes s) {
-  const int np = plan[s.o_hdr + H_STATUS] == 0 ? plan[s.o_hdr + H_NPIECES] : 0;
+  const int np = plan[s.o_hdr + H_STATUS] == 0 ? clamp_count(plan[s.o_hdr + H_NPIECES], s.P_max) : 0;
   const int64_t nchunk = (wv + kCopyChunk - 1) / kCopyChunk;
   const int64_t items = (int64_t)np * nchunk;
   const int32_t* pieces = plan + s.o_pieces;
@@ -477,10 +485,12 @@ __global__ __launch_bounds__(256) void expert_stub_kernel(const int32_t* __restr
     const i32x4 xt = xtab[e];                    // keep, home row, first piece, count
     const u32x4* w = home + (int64_t)e * wv;     // home group, or fallback (remote read)
     if (row < xt.y || row >= xt.y + xt.x) {
-      for (int q = xt.z; q < xt.z + xt.w; ++q) {
+      int q0, q1;
+      piece_range(xt.z, xt.w, s.P_max, &q0, &q1);
+      for (int q = q0; q < q1; ++q) {
         const int32_t* pc = pieces + (int64_t)q * kPieceInts;
         if (row >= pc[P_ROW0] && row < pc[P_ROW0] + pc[P_CNT]) {
-          if (pc[P_SLOT] >= 0 && pc[P_SLOT] < s.slots)
+          if (pc[P_SLOT] >= 0 && pc[P_SLOT] < s.slots && (unsigned)pc[P_R] < (unsigned)s.R)
             w = slotw + ((int64_t)pc[P_R] * s.slots + pc[P_SLOT]) * wv;
           break;
         }
@@ -515,7 +525,7 @@ __global__ __launch_bounds__(kRedThreads) void reduce_kernel(const int32_t* __re
                                                              f32x4* __restrict__ home,
                                                              const f32x4* __restrict__ rep,
                                                              int64_t g4, const moonep_sizes s) {
-  const int nred = plan[s.o_hdr + H_STATUS] == 0 ? plan[s.o_hdr + H_NRED] : 0;
+  const int nred = plan[s.o_hdr + H_STATUS] == 0 ? clamp_count(plan[s.o_hdr + H_NRED], s.E) : 0;
   const int64_t nchunk = (g4 + kRedChunk - 1) / kRedChunk;
   const int64_t items = (int64_t)nred * nchunk;
   const int32_t* red = plan + s.o_red;
@@ -525,8 +535,8 @@ __global__ __launch_bounds__(kRedThreads) void reduce_kernel(const int32_t* __re
     const int64_t c = it - (int64_t)ri * nchunk;
     const int e = red[ri];
     if ((unsigned)e >= (unsigned)s.E) continue;
-    const int q0 = plan[s.o_pfirst + e];
-    const int q1 = q0 + plan[s.o_pnum + e];
+    int q0, q1;
+    piece_range(plan[s.o_pfirst + e], plan[s.o_pnum + e], s.P_max, &q0, &q1);
     f32x4* h = home + (int64_t)e * g4;
     f32x4 acc[kRedU];
 #pragma unroll

@@ -835,7 +835,8 @@ __global__ __launch_bounds__(64) void map_kernel(const int32_t* __restrict__ ids
         } else {
           // the expert's pieces cover [keep, load) in order: j falls in the last piece
           // whose start is <= j.  Eight starts are read per LDS round trip.
-          const int pf = xt[u].z, pn = xt[u].w;
+          // clamped to the piece table: a plan the planner did not write can hold anything
+          const int pf = min(max(xt[u].z, 0), P), pn = min(max(xt[u].w, 0), P - pf);
           const int32_t* pstart = reinterpret_cast<const int32_t*>(ptab_s + pf);
           int n_le = 0;
           for (int p0 = 0; p0 < pn; p0 += 8) {

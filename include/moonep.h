@@ -116,8 +116,9 @@ int moonep_query(int R, int E, int K, int S, int slots, moonep_sizes* out);
  *              zero-filled before its first use: its first word counts the planning
  *              workgroups as they finish, and every call leaves it at zero again, so a
  *              workspace reused call after call (for any sizes) needs no clearing.  A
- *              workspace whose first word is not zero leaves the plan undefined (no
- *              fault: every later kernel bounds its row indices).  Free for other use
+ *              workspace whose first word is not zero leaves the plan undefined; every
+ *              kernel that reads a plan still keeps its accesses inside the plan and the
+ *              buffers it was given, whatever the plan holds.  Free for other use
  *              once the plan's kernels have run on `stream`; two calls whose kernels
  *              overlap in time must not share a workspace
  *   desc       host handle, filled synchronously (sizes + plan_dev)
