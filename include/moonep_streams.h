@@ -1,11 +1,11 @@
 /*
  * moonep_streams.h -- plain 16-byte memory streams that measure, on the same GPU, the
- * ceilings the hot path's kernels are judged against.  Not part of the hot path: the
+ * ceilings the hot path's kernels are measured against.  Not part of the hot path: the
  * benchmark times them beside the path (libmoonep_streams.so).
  *
  * The pages quote no bandwidth or ceiling ("Moonshot AI Open-Sources MoonEP"
  * (tldrocket.com), paragraph 4 and "MoonshotAI/MoonEP 딥다이브" (fiv.co.kr), section 2
- * give only curves against DeepEP); these streams supply the box's own reference points:
+ * give only curves against DeepEP); these streams supply the GPU's own reference points:
  * a linear read, write and copy, and the row mixes of dispatch (one row read, K rows
  * written) and combine (K rows read, one row written) over contiguous or scattered rows.
  *
