@@ -167,7 +167,9 @@ def ceilings(wl, x, recv, out, dev, reps=10):
     """Plain 16-byte streams on the same GPU (libmoonep_streams.so): a linear read, write
     and copy of 4 GiB, and the row mixes of dispatch (one row read, K rows written) and
     combine (K rows read, one row written) on this workload's rows, to contiguous rows and
-    to a seeded random permutation of the rows; GB/s, median of `reps` launches."""
+    to a seeded random permutation of the rows, and the combine backward's (one row and K
+    permuted rows read, those K rows written to a second buffer); GB/s, median of `reps`
+    launches."""
     import numpy as np
     import torch
     from combine_top_id_amd import streams as ST
@@ -205,10 +207,17 @@ def ceilings(wl, x, recv, out, dev, reps=10):
     res["gather_scattered"] = round(fan_rw / med(lambda: ST.gather(perm, K, recv, out)) / 1e3, 1)
     res["read_scattered_rows"] = round(
         fan_w / med(lambda: ST.gather(perm, K, recv, out, write_dst=False)) / 1e3, 1)
+    # the combine backward's mix: a source row and K rows of recv read, the K rows written
+    # to a second receive-shaped buffer
+    upd = torch.empty_like(recv)
+    res["update_scattered"] = round(
+        T * (2 * K + 1) * rb / med(lambda: ST.update(perm, K, x, recv, upd)) / 1e3, 1)
+    del upd
     res["unit"] = "GB/s"
     res["rows"] = (f"{T} source rows x K={K} of {rb} B; random destination rows are a seeded "
-                   f"permutation of {A} rows; each kernel one 64-lane workgroup per row chunk "
-                   f"(2 KB fan-out, 1 KB gather), linear streams 256 lanes per 4 KB")
+                   f"permutation of {A} rows; fan-out and gather one 64-lane workgroup per row "
+                   f"chunk (2 KB fan-out, 1 KB gather), update one workgroup per source row, "
+                   f"linear streams 256 lanes per 4 KB")
     return res
 
 
@@ -481,6 +490,9 @@ def main():
             db / statistics.median(all_d) / 1e3 / ceil["fanout_scattered"], 4)
         ceil["combine_over_gather_scattered"] = round(
             cb / statistics.median(all_c) / 1e3 / ceil["gather_scattered"], 4)
+        if backward is not None:
+            ceil["combine_bwd_over_update_scattered"] = round(
+                backward["combine_bwd_gbps"] / ceil["update_scattered"], 4)
 
     value = args.steps * (db + cb) / timed / 1e9
     res = {

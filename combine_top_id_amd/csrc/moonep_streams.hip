@@ -136,6 +136,50 @@ __global__ __launch_bounds__(64) void gather_kernel(const int32_t* __restrict__ 
   if (write_dst || unlikely_pattern(acc)) __builtin_nontemporal_store(acc, dst + i * nvec + v);
 }
 
+// the combine backward's mix: one workgroup per source row i, its threads holding two
+// vectors of row i and taking its K listed rows in groups of up to 8: every load of the
+// group, one wait, then the group's stores
+__global__ __launch_bounds__(1024) void update_kernel(const int32_t* __restrict__ rows,
+                                                      const u32x4* __restrict__ src,
+                                                      const u32x4* __restrict__ a,
+                                                      u32x4* __restrict__ b, int K, int nvec,
+                                                      int64_t rows_ab) {
+  const int64_t i = blockIdx.x;
+  for (int v0 = threadIdx.x; v0 < nvec; v0 += blockDim.x * 2) {
+    u32x4 sv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int v = v0 + u * blockDim.x;
+      sv[u] = v < nvec ? src[i * nvec + v] : u32x4{0u, 0u, 0u, 0u};
+    }
+    for (int k0 = 0; k0 < K; k0 += 8) {
+      int64_t r[8];
+      u32x4 y[8][2];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        r[j] = k0 + j < K ? rows[i * K + k0 + j] : -1;
+        if (r[j] >= rows_ab) r[j] = -1;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int v = v0 + u * blockDim.x;
+          y[j][u] = r[j] >= 0 && v < nvec ? __builtin_nontemporal_load(a + r[j] * nvec + v)
+                                          : u32x4{0u, 0u, 0u, 0u};
+        }
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int v = v0 + u * blockDim.x;
+          if (r[j] >= 0 && v < nvec) __builtin_nontemporal_store(y[j][u] ^ sv[u], b + r[j] * nvec + v);
+        }
+    }
+  }
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 int status() { return hipGetLastError() == hipSuccess ? 0 : kEHip; }
@@ -246,6 +290,21 @@ int moonep_rows_gather(const int32_t* rows, int64_t n, int K, const void* src, i
   hipLaunchKernelGGL(gather_kernel, dim3((unsigned)(n * nch)), dim3(64), lds, stream, rows,
                      static_cast<const u32x4*>(src), src_rows, static_cast<u32x4*>(dst), K, nvec,
                      nch, write_dst);
+  return status();
+}
+
+int moonep_rows_update(const int32_t* rows, int64_t n, int K, const void* src, const void* a,
+                       void* b, int64_t rows_ab, int row_bytes, hipStream_t stream) {
+  if (!rows || !src || !a || !b || n <= 0 || K < 1 || rows_ab <= 0 || row_bytes <= 0 ||
+      row_bytes % 16 != 0 || !aligned16(src) || !aligned16(a) || !aligned16(b) || n > INT32_MAX)
+    return kEInval;
+  const int nvec = row_bytes / 16;
+  const int half = (nvec + 1) / 2;
+  const int threads = half >= 1024 ? 1024 : (half + 63) / 64 * 64;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(update_kernel, dim3((unsigned)n), dim3(threads), 0, stream, rows,
+                     static_cast<const u32x4*>(src), static_cast<const u32x4*>(a),
+                     static_cast<u32x4*>(b), K, nvec, rows_ab);
   return status();
 }
 

@@ -11,7 +11,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoonep_streams.so")
 SHAPE_WAVE_2K, SHAPE_BLOCK_4K = 0, 1
 EXPORTS = ("moonep_stream_read", "moonep_stream_write", "moonep_stream_copy",
-           "moonep_rows_fanout", "moonep_rows_gather")
+           "moonep_rows_fanout", "moonep_rows_gather", "moonep_rows_update")
 
 _lib = None
 
@@ -29,6 +29,7 @@ def lib():
     L.moonep_stream_copy.argtypes = [vp, vp, i64, i32, i32, vp]
     L.moonep_rows_fanout.argtypes = [vp, i64, i32, vp, vp, i64, i32, i32, vp]
     L.moonep_rows_gather.argtypes = [vp, i64, i32, vp, i64, vp, i32, i32, vp]
+    L.moonep_rows_update.argtypes = [vp, i64, i32, vp, vp, vp, i64, i32, vp]
     for f in EXPORTS:
         getattr(L, f).restype = i32
     _lib = L
@@ -83,3 +84,13 @@ def gather(rows, K, src, dst, write_dst=True):
     _check(lib().moonep_rows_gather(_p(rows), n, K, _p(src), src.shape[0], _p(dst),
                                     src.shape[1] * src.element_size(), int(write_dst), _s(src)),
            "rows_gather")
+
+
+def update(rows, K, src, a, b):
+    """b[rows[i*K + k]] = a[rows[i*K + k]] ^ src[i]; 2-D row tensors, a and b alike."""
+    n = rows.numel() // K
+    assert rows.dtype == torch.int32 and rows.is_contiguous() and src.shape[0] >= n
+    rb = src.shape[1] * src.element_size()
+    assert a.shape == b.shape and a.dtype == b.dtype and a.shape[1] * a.element_size() == rb
+    _check(lib().moonep_rows_update(_p(rows), n, K, _p(src), _p(a), _p(b), a.shape[0], rb, _s(a)),
+           "rows_update")

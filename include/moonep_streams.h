@@ -7,7 +7,8 @@
  * (tldrocket.com), paragraph 4 and "MoonshotAI/MoonEP 딥다이브" (fiv.co.kr), section 2
  * give only curves against DeepEP); these streams supply the GPU's own reference points:
  * a linear read, write and copy, and the row mixes of dispatch (one row read, K rows
- * written) and combine (K rows read, one row written) over contiguous or scattered rows.
+ * written), combine (K rows read, one row written) and the combine backward (one row and
+ * K rows read, the K rows written elsewhere) over contiguous or scattered rows.
  *
  * Conventions: device pointers 16-byte aligned, sizes multiples of 16 bytes, everything
  * enqueued on `stream` and asynchronous.  Return 0, -1 for an invalid argument (nothing
@@ -53,6 +54,13 @@ int moonep_rows_fanout(const int32_t* rows, int64_t n, int K, const void* src, v
  * 9 workgroups per CU when src exceeds 256 MB: the combine kernel's shape and residency. */
 int moonep_rows_gather(const int32_t* rows, int64_t n, int K, const void* src, int64_t src_rows,
                        void* dst, int row_bytes, int write_dst, hipStream_t stream);
+
+/* The combine backward's mix: for i < n, k < K:  b row r = a row r XOR src row i, where
+ * r = rows[i*K + k] (rows outside [0, rows_ab) skipped); a and b have rows_ab rows.  One
+ * workgroup per source row, its K rows taken in groups of up to 8 (every load of the
+ * group, one wait, the non-temporal stores): the combine backward kernel's shape. */
+int moonep_rows_update(const int32_t* rows, int64_t n, int K, const void* src, const void* a,
+                       void* b, int64_t rows_ab, int row_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -159,6 +159,10 @@ int main(void) {
   EXPECT(moonep_rows_fanout(fake, 4, 2, NULL, fake, 8, 64, 1, 0) == -1);
   EXPECT(moonep_rows_gather(fake, 4, 2, fake, 8, fake, 24, 1, 0) == -1);
   EXPECT(moonep_rows_gather(fake, 0, 2, fake, 8, fake, 64, 1, 0) == -1);
+  EXPECT(moonep_rows_update(fake, 4, 2, fake, fake, fake, 8, 24, 0) == -1);   /* not 16 B */
+  EXPECT(moonep_rows_update(fake, 4, 0, fake, fake, fake, 8, 64, 0) == -1);   /* K < 1 */
+  EXPECT(moonep_rows_update(fake, 4, 2, fake, NULL, fake, 8, 64, 0) == -1);
+  EXPECT(moonep_rows_update(fake, 4, 2, fake, fake, fake, 0, 64, 0) == -1);   /* no rows */
 
   printf("asan host %s: %d checks, %d failed\n", g_fails ? "FAILED" : "ok", g_checks, g_fails);
   return g_fails ? 1 : 0;

@@ -5,7 +5,9 @@ Each stream runs on small buffers whose results are checked in full: the copy is
 copy, the write stores its documented pattern, the read leaves its sink alone, the row
 fan-out writes each source row to every listed row and nothing else, and the row gather
 writes the XOR of the listed rows (rows outside the buffer skipped) or nothing at all.
-The gather's residency-capped launch (a source above 256 MB) is covered too."""
+The gather's residency-capped launch (a source above 256 MB) is covered too, and the
+row update (the combine backward's mix) writes each listed row of b as that row of a XOR
+its source row."""
 
 import numpy as np
 import pytest
@@ -108,3 +110,23 @@ def test_row_gather(row_vec, K, nrows):
     ST.gather(torch.from_numpy(rows).cuda(), K, src, dst, write_dst=False)
     torch.cuda.synchronize()
     assert (dst == 3).all()
+
+
+@pytest.mark.parametrize("row_vec,K,nrows", [(64, 8, 400), (200, 3, 400), (896, 8, 400), (1100, 10, 500),
+                                             (2100, 4, 200)])
+def test_row_update(row_vec, K, nrows):
+    n = 37
+    rows = _row_list(n, K, nrows, 13)
+    src = _rand_rows(n, row_vec, 41)
+    a = _rand_rows(nrows, row_vec, 43)
+    b = torch.zeros_like(a)
+    ST.update(torch.from_numpy(rows).cuda(), K, src, a, b)
+    torch.cuda.synchronize()
+    s_np, a_np = src.cpu().numpy(), a.cpu().numpy()
+    want = np.zeros_like(a_np)
+    for i in range(n):
+        for k in range(K):
+            r = rows[i * K + k]
+            if 0 <= r < nrows:
+                want[r] = a_np[r] ^ s_np[i]
+    assert (b.cpu().numpy() == want).all()
