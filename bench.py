@@ -221,6 +221,30 @@ def ceilings(wl, x, recv, out, dev, reps=10):
     return res
 
 
+def device_facts(dev):
+    """What the figures depend on beyond the code: the GPU and its HBM (read-only queries).
+    Boxes of the same model differ; scattered-row writes in particular ran about 20%
+    faster on one box than on the others measured."""
+    import re
+    import shutil
+    import subprocess
+    import torch
+    p = torch.cuda.get_device_properties(dev)
+    facts = {"arch": p.gcnArchName, "compute_units": p.multi_processor_count,
+             "memory_gb": round(p.total_memory / 1e9, 1), "memory_vendor": None, "mclk_mhz": None}
+    smi = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
+    try:
+        out = subprocess.run([smi, "--showmemvendor", "--showclocks"], capture_output=True,
+                             text=True, timeout=30).stdout
+        v = re.search(r"memory vendor:\s*(\S+)", out)
+        m = re.search(r"mclk clock level:.*\((\d+)\s*Mhz\)", out)
+        facts["memory_vendor"] = v.group(1) if v else None
+        facts["mclk_mhz"] = int(m.group(1)) if m else None
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return facts
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -536,6 +560,7 @@ def main():
         "plan_us_median": round(statistics.median([r["plan_us"] for r in rows]), 2),
         "plan_us_back_to_back": round(plan_b2b_us, 2),
         "ceilings": ceil,
+        "device": device_facts(dev),
         "backward": backward,
         "prefetch": prefetch,
         "zero_copy_ab": staged,
